@@ -1,0 +1,132 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) O(N)-memory fused attention library.
+ *
+ * The library computes scaled-dot-product attention for training without ever
+ * materialising an (N, N) score or mask matrix.  The forward saves only the
+ * output O and the per-row log-sum-exp; the backward recomputes the softmax
+ * tile by tile from Q, K and that log-sum-exp (mlx-train-perf 0.5.1 README,
+ * section "Flash-attention training path": O(N) saved state, tiles recomputed).
+ * Masking is causal, optionally block-diagonal by a per-token segment id, so a
+ * token attends another only when both belong to the same packed sequence
+ * (same README, section "Sequence packing"; mlx-train-perf changelog, section
+ * "Added": PACKED variants of the forward, dQ and dK/dV kernels driven by an
+ * O(N) per-token segment id, never a materialised mask).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, contiguous, row-major (B, H, N, D) device buffers of
+ *     the element type `dtype` (bf16 or fp32), D in {64, 128}, as in the
+ *     README's "If you maintain a trainer" section ((B, H, N, D) with head_dim
+ *     in {64, 96, 128}; 96 is not built yet and is refused).
+ *   - `lse` is a (B, H, N) fp32 device buffer holding the natural-log
+ *     log-sum-exp of scale * q_i . k_j over the keys row i may see.
+ *   - `seg` is NULL (no packing) or a (B, N) int32 device buffer of segment ids
+ *     that must be non-decreasing along each row (contiguous segments).  Query
+ *     i sees key j iff (causal == 0 or j <= i) and (seg == NULL or
+ *     seg[b][i] == seg[b][j]).  A row whose ids decrease gives unspecified
+ *     values but every access stays in bounds; fa_check_seg validates a host
+ *     copy, and the int32 at workspace offset 0 is set non-zero by the device
+ *     when a decrease is seen.
+ *   - Tensor pointers must be 16-byte aligned, lse and seg 4-byte aligned, the
+ *     workspace 256-byte aligned.
+ *   - The caller owns every buffer, including the workspace (size from
+ *     fa_workspace_bytes).  The library never allocates device memory and keeps
+ *     no state between calls beyond a per-device architecture check.
+ *   - Calls are asynchronous on `stream` (a hipStream_t of the current device;
+ *     NULL means the default stream).  Outputs are overwritten, never
+ *     accumulated; inputs are only read.  Two calls that share a workspace
+ *     must be ordered on one stream.
+ *   - Errors: arguments are validated on the host before any HIP call; a
+ *     refused call returns a non-zero fa_status and launches nothing
+ *     ("typed refusals, never silent fallbacks": README, "If you maintain a
+ *     trainer").  FA_ERR_HIP reports a failed launch.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,       /* a required pointer is NULL */
+    FA_ERR_SHAPE = 2,      /* B, H or N < 1, or sizes beyond the supported range */
+    FA_ERR_HEAD_DIM = 3,   /* D not in {64, 128} */
+    FA_ERR_DTYPE = 4,      /* dtype is neither FA_BF16 nor FA_FP32 (fp16 is refused) */
+    FA_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than fa_workspace_bytes() */
+    FA_ERR_ALIGN = 6,      /* a pointer violates the alignment rules above */
+    FA_ERR_SCALE = 7,      /* scale is not a finite positive number */
+    FA_ERR_SEG = 8,        /* fa_check_seg: ids decrease somewhere along a row */
+    FA_ERR_HIP = 9,        /* a HIP call or kernel launch failed */
+    FA_ERR_DEVICE = 10     /* the current device is not a gfx950 GPU (or none) */
+} fa_status;
+
+typedef enum fa_dtype {
+    FA_BF16 = 0,
+    FA_FP32 = 1
+} fa_dtype;
+
+/* Largest supported sequence length (rows per head). */
+#define FA_MAX_N (1 << 24)
+
+/*
+ * Bytes of workspace fa_fwd (for_bwd = 0) or fa_bwd (for_bwd = 1) needs for
+ * this shape.  O(B*H*N): 256 bytes of flags, plus for the backward two fp32
+ * (B, H, N) arrays (the row sums D_i = dO_i . O_i and log2-domain LSE), plus
+ * with has_seg two per-tile range tables of B * ceil(N/32) int32 pairs.
+ * Returns 0 for shapes fa_fwd / fa_bwd would refuse.
+ */
+size_t fa_workspace_bytes(int B, int H, int N, int D, int has_seg, int for_bwd);
+
+/*
+ * Forward pass.  Writes o = softmax(scale * q k^T, masked) v and lse.
+ *   q, k, v : (B, H, N, D) `dtype`, read only.
+ *   seg     : (B, N) int32 or NULL.
+ *   scale   : softmax scale (typically 1/sqrt(D)), finite and > 0.
+ *   causal  : non-zero for causal masking.
+ *   o       : (B, H, N, D) `dtype`, written.
+ *   lse     : (B, H, N) fp32, written.
+ *   ws      : workspace of at least fa_workspace_bytes(B,H,N,D,seg!=NULL,0)
+ *             bytes (may be NULL when that is 0).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, const int32_t* seg,
+                 float scale, int causal, void* o, float* lse,
+                 int B, int H, int N, int D, fa_dtype dtype,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward pass from the output gradient dO (no gradient flows into lse).
+ * Recomputes P = exp(scale q k^T - lse) tile by tile and writes
+ *   dq = scale * dS k,  dk = scale * dS^T q,  dv = P^T dO,
+ * with dS = P * (dO v^T - D_i) and D_i = dO_i . O_i taken from the stored o.
+ *   q, k, v, o, dO : (B, H, N, D) `dtype`, read only; o and lse come from
+ *                    fa_fwd with the same q, k, v, seg, scale and causal.
+ *   lse            : (B, H, N) fp32 from fa_fwd.
+ *   seg, scale, causal : must equal the forward's.
+ *   dq, dk, dv     : (B, H, N, D) `dtype`, written.
+ *   ws             : workspace of at least fa_workspace_bytes(..., 1) bytes.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dO, const float* lse, const int32_t* seg,
+                 float scale, int causal, void* dq, void* dk, void* dv,
+                 int B, int H, int N, int D, fa_dtype dtype,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Host-side precondition check of a HOST copy of seg: FA_OK when every row is
+ * non-decreasing, FA_ERR_SEG otherwise, FA_ERR_NULL / FA_ERR_SHAPE for bad
+ * arguments.  Makes no HIP call.
+ */
+fa_status fa_check_seg(const int32_t* host_seg, int B, int N);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(fa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

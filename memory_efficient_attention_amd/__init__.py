@@ -1,0 +1,190 @@
+"""Python binding of the gfx950 O(N)-memory attention library (libfa.so).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels.  PyTorch provides device memory (output and workspace tensors)
+and the current HIP stream.  The functions carry the C entry points' names:
+
+    o, lse = fa_fwd(q, k, v, seg=None, scale=None, causal=True)
+    dq, dk, dv = fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True)
+
+q, k, v, o, do are contiguous (B, H, N, D) CUDA tensors (torch.bfloat16 or
+torch.float32, D in {64, 128}); seg is None or a contiguous (B, N) int32 CUDA
+tensor of non-decreasing segment ids; lse is (B, H, N) float32.  A refused
+call raises FaError naming the reason; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_workspace_bytes", "fa_check_seg",
+           "fa_status_string", "flash_attention", "library_path", "load_library",
+           "FA_BF16", "FA_FP32"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfa.so")
+FA_BF16, FA_FP32 = 0, 1
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A refused or failed library call; ``status`` is the fa_status code."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (fa_status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfa.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m memory_efficient_attention_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_workspace_bytes.restype = sz
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, f, i, vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_check_seg.argtypes = [vp, i, i]
+    lib.fa_check_seg.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_workspace_bytes(B: int, H: int, N: int, D: int, has_seg: bool, for_bwd: bool) -> int:
+    return int(load_library().fa_workspace_bytes(B, H, N, D, int(bool(has_seg)), int(bool(for_bwd))))
+
+
+def fa_check_seg(seg) -> None:
+    """Validate a host (CPU) copy of seg; raises FaError if ids decrease in a row."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(seg.cpu() if hasattr(seg, "cpu") else seg, dtype=np.int32))
+    if a.ndim != 2:
+        raise ValueError("seg must be (B, N)")
+    st = load_library().fa_check_seg(a.ctypes.data, a.shape[0], a.shape[1])
+    if st:
+        raise FaError(st, "fa_check_seg")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_FP32
+    return 99   # the library refuses it with FA_ERR_DTYPE
+
+
+def _check_tensor(name, t, shape, dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _seg_ptr(seg, B, N):
+    import torch
+    if seg is None:
+        return None
+    _check_tensor("seg", seg, (B, N), torch.int32)
+    return seg.data_ptr()
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def fa_fwd(q, k, v, seg=None, scale=None, causal=True, out=None, lse=None, workspace=None):
+    """Forward pass; returns (o, lse)."""
+    import torch
+    B, H, N, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, (B, H, N, D), q.dtype)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("o", o, (B, H, N, D), q.dtype)
+    _check_tensor("lse", lse_t, (B, H, N), torch.float32)
+    seg_p = _seg_ptr(seg, B, N)
+    lib = load_library()
+    nbytes = lib.fa_workspace_bytes(B, H, N, D, int(seg is not None), 0)
+    ws = workspace
+    if nbytes and (ws is None or ws.numel() < nbytes):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_p, ctypes.c_float(scale),
+                    int(bool(causal)), o.data_ptr(), lse_t.data_ptr(), B, H, N, D,
+                    _dtype_code(q), ws.data_ptr() if (ws is not None and nbytes) else None,
+                    nbytes, _stream())
+    if st:
+        raise FaError(st, "fa_fwd")
+    return o, lse_t
+
+
+def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=None, dv=None,
+           workspace=None):
+    """Backward pass from dO; returns (dq, dk, dv)."""
+    import torch
+    B, H, N, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, t, (B, H, N, D), q.dtype)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, (B, H, N, D), q.dtype)
+    seg_p = _seg_ptr(seg, B, N)
+    lib = load_library()
+    nbytes = lib.fa_workspace_bytes(B, H, N, D, int(seg is not None), 1)
+    ws = workspace
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                    lse.data_ptr(), seg_p, ctypes.c_float(scale), int(bool(causal)),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, _dtype_code(q),
+                    ws.data_ptr(), nbytes, _stream())
+    if st:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def flash_attention(q, k, v, scale=None, causal=True, segments=None):
+    """Differentiable attention through fa_fwd / fa_bwd (torch.autograd.Function)."""
+    import torch
+
+    class _Fn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q_, k_, v_):
+            o, lse = fa_fwd(q_, k_, v_, segments, scale, causal)
+            ctx.save_for_backward(q_, k_, v_, o, lse)
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q_, k_, v_, o, lse = ctx.saved_tensors
+            return fa_bwd(q_, k_, v_, o, do.contiguous(), lse, segments, scale, causal)
+
+    return _Fn.apply(q, k, v)

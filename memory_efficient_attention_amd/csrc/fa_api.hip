@@ -1,0 +1,241 @@
+// C ABI: argument validation, workspace layout and kernel dispatch.
+//
+// Every refusal is decided on the host before any HIP call ("typed refusals,
+// never silent fallbacks": mlx-train-perf 0.5.1 README, "If you maintain a
+// trainer"), so a refused call launches nothing.  The library allocates no
+// memory; the caller passes a workspace sized by fa_workspace_bytes().
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+#define FA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMinTile = 32;   // tables are sized for the smallest tile, so any tile config fits
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Layout {
+  size_t flag = 0, delta = 0, lse2 = 0, qtab = 0, ktab = 0, total = 0;
+};
+
+bool shape_ok(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1 || N > FA_MAX_N) return false;
+  const long long rows = (long long)B * H * N;
+  return rows <= INT_MAX;   // B*H*ceil(N/32) workgroups and B*H*N rows fit in int
+}
+
+Layout layout(int B, int H, int N, bool has_seg, bool for_bwd) {
+  Layout L;
+  if (!for_bwd && !has_seg) return L;   // plain forward needs no workspace
+  size_t off = kAlign;                  // flag word(s)
+  if (for_bwd) {
+    const size_t vec = align_up((size_t)B * H * N * sizeof(float));
+    L.delta = off;
+    off += vec;
+    L.lse2 = off;
+    off += vec;
+  }
+  if (has_seg) {
+    const size_t tab = align_up((size_t)B * ((N + kMinTile - 1) / kMinTile) * sizeof(int2));
+    L.qtab = off;
+    off += tab;
+    L.ktab = off;
+    off += tab;
+  }
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
+std::mutex g_mu;
+signed char g_dev_ok[64];
+
+fa_status device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return FA_ERR_DEVICE;
+  }
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_dev_ok[dev] == 1) return FA_OK;
+    if (g_dev_ok[dev] == 2) return FA_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return FA_ERR_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_dev_ok[dev] = ok ? 1 : 2;
+  }
+  return ok ? FA_OK : FA_ERR_DEVICE;
+}
+
+fa_status common_checks(int B, int H, int N, int D, fa_dtype dtype, float scale) {
+  if (!shape_ok(B, H, N)) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_DTYPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+float log2e_scale(float scale) { return (float)((double)scale * 1.4426950408889634); }
+
+}  // namespace
+
+FA_API size_t fa_workspace_bytes(int B, int H, int N, int D, int has_seg, int for_bwd) {
+  if (!shape_ok(B, H, N) || (D != 64 && D != 128)) return 0;
+  return layout(B, H, N, has_seg != 0, for_bwd != 0).total;
+}
+
+FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32_t* seg, float scale,
+                        int causal, void* o, float* lse, int B, int H, int N, int D, fa_dtype dtype,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (fa_status st = common_checks(B, H, N, D, dtype, scale)) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(seg, 4))
+    return FA_ERR_ALIGN;
+  const Layout L = layout(B, H, N, seg != nullptr, false);
+  if (L.total > 0) {
+    if (!ws || ws_bytes < L.total) return FA_ERR_WORKSPACE;
+    if (!aligned(ws, kAlign)) return FA_ERR_ALIGN;
+  }
+  if (fa_status st = device_ok()) return st;
+  (void)hipGetLastError();
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const int dt = dtype == FA_BF16 ? 0 : 1;
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.seg = seg;
+  p.qtab = seg ? (const int2*)(w + L.qtab) : nullptr;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.nqt = (N + fa::FWD_BM - 1) / fa::FWD_BM;
+  p.scale = scale;
+  p.c = log2e_scale(scale);
+  if (seg) {
+    if (fa::launch_seg_check(seg, B, N, (int32_t*)(w + L.flag), s) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_qtile_table(seg, B, N, fa::FWD_BM, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
+        hipSuccess)
+      return FA_ERR_HIP;
+  }
+  if (fa::launch_fwd(p, dt, D, causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                        const float* lse, const int32_t* seg, float scale, int causal, void* dq, void* dk,
+                        void* dv, int B, int H, int N, int D, fa_dtype dtype, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (fa_status st = common_checks(B, H, N, D, dtype, scale)) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(seg, 4))
+    return FA_ERR_ALIGN;
+  const Layout L = layout(B, H, N, seg != nullptr, true);
+  if (!ws || ws_bytes < L.total) return FA_ERR_WORKSPACE;
+  if (!aligned(ws, kAlign)) return FA_ERR_ALIGN;
+  if (fa_status st = device_ok()) return st;
+  (void)hipGetLastError();
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const int dt = dtype == FA_BF16 ? 0 : 1;
+  float* delta = (float*)(w + L.delta);
+  float* lse2 = (float*)(w + L.lse2);
+
+  if (seg) {
+    if (fa::launch_seg_check(seg, B, N, (int32_t*)(w + L.flag), s) != hipSuccess) return FA_ERR_HIP;
+    if (fa::launch_qtile_table(seg, B, N, fa::FWD_BM, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
+        hipSuccess)
+      return FA_ERR_HIP;
+    if (fa::launch_ktile_table(seg, B, N, fa::DKV_BN, fa::QRY_TILE, causal != 0, (int2*)(w + L.ktab), s) !=
+        hipSuccess)
+      return FA_ERR_HIP;
+  }
+
+  fa::PreParams pp{};
+  pp.o = o;
+  pp.dO = dO;
+  pp.lse = lse;
+  pp.delta = delta;
+  pp.lse2 = lse2;
+  pp.rows = (long long)B * H * N;
+  if (fa::launch_bwd_pre(pp, dt, D, s) != hipSuccess) return FA_ERR_HIP;
+
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dO = dO;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.lse2 = lse2;
+  p.delta = delta;
+  p.seg = seg;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.scale = scale;
+  p.c = log2e_scale(scale);
+
+  p.tab = seg ? (const int2*)(w + L.ktab) : nullptr;
+  p.ntiles = (N + fa::DKV_BN - 1) / fa::DKV_BN;
+  if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+
+  p.tab = seg ? (const int2*)(w + L.qtab) : nullptr;
+  p.ntiles = (N + fa::FWD_BM - 1) / fa::FWD_BM;
+  if (fa::launch_bwd_dq(p, dt, D, causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+FA_API fa_status fa_check_seg(const int32_t* host_seg, int B, int N) {
+  if (!host_seg) return FA_ERR_NULL;
+  if (B < 1 || N < 1 || N > FA_MAX_N) return FA_ERR_SHAPE;
+  for (long long b = 0; b < B; ++b) {
+    const int32_t* r = host_seg + b * N;
+    for (int i = 0; i + 1 < N; ++i)
+      if (r[i] > r[i + 1]) return FA_ERR_SEG;
+  }
+  return FA_OK;
+}
+
+FA_API const char* fa_status_string(fa_status status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H or N out of range";
+    case FA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be bf16 or fp32";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_workspace_bytes()";
+    case FA_ERR_ALIGN: return "pointer misaligned (tensors 16 B, lse/seg 4 B, workspace 256 B)";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_SEG: return "segment ids decrease along a row";
+    case FA_ERR_HIP: return "HIP launch failed";
+    case FA_ERR_DEVICE: return "current device is not a gfx950 GPU";
+  }
+  return "unknown status";
+}

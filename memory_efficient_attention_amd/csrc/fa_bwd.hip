@@ -1,0 +1,422 @@
+// Backward kernels: the D_i preprocess, dQ, and dK/dV.
+//
+// The backward keeps O(N) state and recomputes the probability tiles from Q,
+// K and the saved log-sum-exp (mlx-train-perf 0.5.1 README, section
+// "Flash-attention training path"), with causal and packed block-diagonal
+// masking (changelog "Added": PACKED variants of the dQ and dK/dV kernels;
+// README "Sequence packing": the dK/dV pass bounds its query walk at each key
+// block's segment end rather than masking cross-segment work after computing
+// it).  With P = exp(scale Q K^T - LSE) and dP = dO V^T, the softmax
+// Jacobian gives dS = P * (dP - D) with D_i = sum_j P_ij dP_ij = dO_i . O_i;
+// then dQ = scale dS K, dK = scale dS^T Q and dV = P^T dO.
+//
+// No atomics: dQ is accumulated in registers over key tiles by the workgroup
+// owning a query tile, dK and dV over query tiles by the workgroup owning a
+// key tile, so results are deterministic run to run.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+// ---------------------------------------------------------------- preprocess
+// delta[r] = sum_d dO[r, d] * O[r, d] (O as stored), lse2[r] = lse[r] * log2(e).
+// LPR lanes share one row, each reading 16 contiguous bytes of O and dO.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
+  constexpr int LPR = D * (int)sizeof(T) / 16;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid / LPR;
+  const int sub = (int)(gid % LPR);
+  float acc = 0.f;
+  if (row < p.rows) {
+    const size_t e = (size_t)row * D + (size_t)sub * (16 / sizeof(T));
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 o = *(const bf16x8*)((const T*)p.o + e);
+      const bf16x8 g = *(const bf16x8*)((const T*)p.dO + e);
+      const f32x8 of = __builtin_convertvector(o, f32x8), gf = __builtin_convertvector(g, f32x8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = fmaf(of[i], gf[i], acc);
+    } else {
+      const f32x4 o = *(const f32x4*)((const T*)p.o + e);
+      const f32x4 g = *(const f32x4*)((const T*)p.dO + e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf(o[i], g[i], acc);
+    }
+  }
+#pragma unroll
+  for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
+  if (row < p.rows && sub == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+// One workgroup = 4 waves x 32 queries; walks the key tiles the query tile can
+// see.  Per tile: S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T held in registers),
+// P^T and dS^T in registers, dQ^T += K^T dS^T with K^T through the transposing
+// LDS read of the K tile.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
+  constexpr int NW = FWD_WAVES, NT = NW * 64, BM = FWD_BM, BN = KEY_TILE;
+  constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
+  constexpr int TILE = BN * D * (int)sizeof(T);
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE + 2 * BN * 4];
+  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int N = p.N;
+  const int nqt = p.ntiles;
+
+  const int total = p.B * p.H * nqt;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int bh = L / nqt;
+  const int qt = nqt - 1 - (L - bh * nqt);
+  const int b = bh / p.H;
+  const size_t off = (size_t)bh * N * D;
+  const T* gq = (const T*)p.q + off;
+  const T* gk = (const T*)p.k + off;
+  const T* gv = (const T*)p.v + off;
+  const T* gdo = (const T*)p.dO + off;
+  const int32_t* seg = p.seg ? p.seg + (size_t)b * N : nullptr;
+  const bool packed = seg != nullptr;
+
+  const int q0 = qt * BM;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + col;
+  const int qc = min(qi, N - 1);
+  const int qlast = min(qw0 + 31, N - 1);
+
+  int kt_lo = 0, kt_hi;
+  if (packed) {
+    const int2 r = p.tab[(size_t)b * nqt + qt];
+    kt_lo = r.x;
+    kt_hi = r.y;
+  } else {
+    kt_hi = ((CAUSAL ? min(q0 + BM, N) : N) - 1) / BN;
+  }
+
+  frag_t<T> qf[KS], dof[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = gfrag_row<T, D>(gq, qc, 2 * ks + h);
+    dof[ks] = gfrag_row<T, D>(gdo, qc, 2 * ks + h);
+  }
+  const float lse2 = p.lse2[(size_t)bh * N + qc];
+  const float dlt = p.delta[(size_t)bh * N + qc];
+  int segq = 0, segq_first = 0, segq_last = 0;
+  if (packed) {
+    segq = seg[qc];
+    segq_first = seg[min(qw0, N - 1)];
+    segq_last = seg[qlast];
+  }
+  const float c = p.c;
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
+
+  auto stage = [&](int kt, int buf) {
+    stage_tile<T, BN, D, NT>(smem + buf * TILE, gk, kt * BN, N, wave, lane);
+    stage_tile<T, BN, D, NT>(smem + (2 + buf) * TILE, gv, kt * BN, N, wave, lane);
+    if (packed) stage_vec<BN>(smem + 4 * TILE + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
+  };
+
+  if (kt_lo <= kt_hi) stage(kt_lo, 0);
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    const int buf = (kt - kt_lo) & 1;
+    wait_loads();
+    __syncthreads();
+    if (kt < kt_hi) stage(kt + 1, buf ^ 1);
+
+    const FA_LDS char* Ks = smem + buf * TILE;
+    const FA_LDS char* Vs = smem + (2 + buf) * TILE;
+    const FA_LDS int* segk = (const FA_LDS int*)(smem + 4 * TILE + buf * BN * 4);
+    const int k0 = kt * BN;
+    const int klast = min(k0 + BN, N) - 1;
+
+    bool skip = qw0 >= N;
+    if (CAUSAL) skip = skip || k0 > qlast;
+    bool full = (k0 + BN <= N) && (!CAUSAL || k0 + BN - 1 <= qw0);
+    if (packed) {
+      const int sk0 = segk[0], skl = segk[klast - k0];
+      skip = skip || skl < segq_first || (!CAUSAL && sk0 > segq_last);
+      full = full && (min(sk0, segq_first) == max(skl, segq_last));
+    }
+    if (skip) continue;
+
+    f32x16 sacc[KB], dpacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sacc[kb] = f32x16{};
+      dpacc[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        mma(sacc[kb], frag_row<T, D>(Ks, 32 * kb + col, 2 * ks + h), qf[ks]);
+        mma(dpacc[kb], frag_row<T, D>(Vs, 32 * kb + col, 2 * ks + h), dof[ks]);
+      }
+    }
+
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 32 * kb + 8 * j + 4 * h;
+        i32x4 sk = (packed && !full) ? *(const FA_LDS i32x4*)(segk + kr) : i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = sacc[kb][4 * j + i];
+          if (!full) {
+            const int key = k0 + kr + i;
+            const bool vis = key < N && (!CAUSAL || key <= qi) && (!packed || sk[i] == segq);
+            if (!vis) s = -INFINITY;
+          }
+          const float pv = exp2_fast(fmaf(s, c, -lse2));
+          sacc[kb][4 * j + i] = pv * (dpacc[kb][4 * j + i] - dlt);
+        }
+      }
+    }
+
+    frag_t<T> dsf[KB][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      dsf[kb][0] = acc_frag<T>(sacc[kb], 0);
+      dsf[kb][1] = acc_frag<T>(sacc[kb], 1);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+          mma(dqacc[db], frag_col<T, D>(Ks, 32 * kb + 16 * kc, 32 * db, lane), dsf[kb][kc]);
+  }
+
+  if (qi < N) store_rows<T, D>((T*)p.dq + off, qi, dqacc, p.scale, lane);
+}
+
+// ---------------------------------------------------------------- dK / dV
+// One workgroup = 4 waves x 32 keys; walks the query tiles that can see the
+// key tile.  Per tile: S = Q K^T and dP = dO V^T (K^T, V^T held in registers;
+// the accumulator columns are keys, rows queries), P and dS in registers,
+// dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T through the transposing
+// LDS read.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p) {
+  constexpr int NW = DKV_WAVES, NT = NW * 64, BNK = DKV_BN, BMQ = QRY_TILE;
+  constexpr int KS = D / 16, DB = D / 32, QB = BMQ / 32;
+  constexpr int TILE = BMQ * D * (int)sizeof(T);
+  constexpr int VEC = BMQ * 4;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE + 6 * VEC];
+  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  // layout: Q[2] | dO[2] | lse2[2] | delta[2] | seg[2]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int N = p.N;
+  const int nkt = p.ntiles;
+
+  const int total = p.B * p.H * nkt;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int bh = L / nkt;
+  const int kt = L - bh * nkt;       // causal: key tile 0 sees the most queries
+  const int b = bh / p.H;
+  const size_t off = (size_t)bh * N * D;
+  const T* gq = (const T*)p.q + off;
+  const T* gk = (const T*)p.k + off;
+  const T* gv = (const T*)p.v + off;
+  const T* gdo = (const T*)p.dO + off;
+  const float* glse2 = p.lse2 + (size_t)bh * N;
+  const float* gdelta = p.delta + (size_t)bh * N;
+  const int32_t* seg = p.seg ? p.seg + (size_t)b * N : nullptr;
+  const bool packed = seg != nullptr;
+
+  const int k0 = kt * BNK;
+  const int kw0 = k0 + wave * 32;
+  const int kj = kw0 + col;
+  const int kc_ = min(kj, N - 1);
+  const int klast = min(kw0 + 31, N - 1);
+
+  int qt_lo, qt_hi;
+  if (packed) {
+    const int2 r = p.tab[(size_t)b * nkt + kt];
+    qt_lo = r.x;
+    qt_hi = r.y;
+  } else {
+    qt_lo = CAUSAL ? k0 / BMQ : 0;
+    qt_hi = (N - 1) / BMQ;
+  }
+
+  frag_t<T> kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = gfrag_row<T, D>(gk, kc_, 2 * ks + h);
+    vf[ks] = gfrag_row<T, D>(gv, kc_, 2 * ks + h);
+  }
+  int segk = 0, segk_first = 0, segk_last = 0;
+  if (packed) {
+    segk = seg[kc_];
+    segk_first = seg[min(kw0, N - 1)];
+    segk_last = seg[klast];
+  }
+  const float c = p.c;
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+
+  auto stage = [&](int qt, int buf) {
+    const int r0 = qt * BMQ;
+    stage_tile<T, BMQ, D, NT>(smem + buf * TILE, gq, r0, N, wave, lane);
+    stage_tile<T, BMQ, D, NT>(smem + (2 + buf) * TILE, gdo, r0, N, wave, lane);
+    stage_vec<BMQ>(smem + 4 * TILE + buf * VEC, glse2, r0, N, wave, 0, lane);
+    stage_vec<BMQ>(smem + 4 * TILE + (2 + buf) * VEC, gdelta, r0, N, wave, 1 % NW, lane);
+    if (packed) stage_vec<BMQ>(smem + 4 * TILE + (4 + buf) * VEC, seg, r0, N, wave, 2 % NW, lane);
+  };
+
+  if (qt_lo <= qt_hi) stage(qt_lo, 0);
+  for (int qt = qt_lo; qt <= qt_hi; ++qt) {
+    const int buf = (qt - qt_lo) & 1;
+    wait_loads();
+    __syncthreads();
+    if (qt < qt_hi) stage(qt + 1, buf ^ 1);
+
+    const FA_LDS char* Qs = smem + buf * TILE;
+    const FA_LDS char* dOs = smem + (2 + buf) * TILE;
+    const FA_LDS float* l2s = (const FA_LDS float*)(smem + 4 * TILE + buf * VEC);
+    const FA_LDS float* dls = (const FA_LDS float*)(smem + 4 * TILE + (2 + buf) * VEC);
+    const FA_LDS int* sqs = (const FA_LDS int*)(smem + 4 * TILE + (4 + buf) * VEC);
+    const int q0 = qt * BMQ;
+    const int qlast = min(q0 + BMQ, N) - 1;
+
+    bool skip = kw0 >= N;
+    if (CAUSAL) skip = skip || qlast < kw0;
+    bool full = (q0 + BMQ <= N) && (kw0 + 31 < N) && (!CAUSAL || q0 >= kw0 + 31);
+    if (packed) {
+      const int sq0 = sqs[0], sql = sqs[qlast - q0];
+      skip = skip || sq0 > segk_last || (!CAUSAL && sql < segk_first);
+      full = full && (min(sq0, segk_first) == max(sql, segk_last));
+    }
+    if (skip) continue;
+
+    f32x16 sacc[QB], dpacc[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      sacc[qb] = f32x16{};
+      dpacc[qb] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        mma(sacc[qb], frag_row<T, D>(Qs, 32 * qb + col, 2 * ks + h), kf[ks]);
+        mma(dpacc[qb], frag_row<T, D>(dOs, 32 * qb + col, 2 * ks + h), vf[ks]);
+      }
+    }
+
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qr = 32 * qb + 8 * j + 4 * h;
+        const f32x4 l2 = *(const FA_LDS f32x4*)(l2s + qr);
+        const f32x4 dl = *(const FA_LDS f32x4*)(dls + qr);
+        i32x4 sq = (packed && !full) ? *(const FA_LDS i32x4*)(sqs + qr) : i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = sacc[qb][4 * j + i];
+          if (!full) {
+            const int q = q0 + qr + i;
+            const bool vis = q < N && kj < N && (!CAUSAL || kj <= q) && (!packed || sq[i] == segk);
+            if (!vis) s = -INFINITY;
+          }
+          const float pv = exp2_fast(fmaf(s, c, -l2[i]));
+          sacc[qb][4 * j + i] = pv;
+          dpacc[qb][4 * j + i] = pv * (dpacc[qb][4 * j + i] - dl[i]);
+        }
+      }
+    }
+
+    frag_t<T> pf[QB][2], dsf[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        pf[qb][kc] = acc_frag<T>(sacc[qb], kc);
+        dsf[qb][kc] = acc_frag<T>(dpacc[qb], kc);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          mma(dvacc[db], frag_col<T, D>(dOs, 32 * qb + 16 * kc, 32 * db, lane), pf[qb][kc]);
+          mma(dkacc[db], frag_col<T, D>(Qs, 32 * qb + 16 * kc, 32 * db, lane), dsf[qb][kc]);
+        }
+  }
+
+  if (kj < N) {
+    store_rows<T, D>((T*)p.dk + off, kj, dkacc, p.scale, lane);
+    store_rows<T, D>((T*)p.dv + off, kj, dvacc, 1.f, lane);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T, int D>
+static hipError_t launch_pre_t(const PreParams& p, hipStream_t s) {
+  constexpr int LPR = D * (int)sizeof(T) / 16;
+  const long long threads = p.rows * LPR;
+  const long long blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const PreParams& p, int dtype, int D, hipStream_t s) {
+  if (dtype == 0) return D == 128 ? launch_pre_t<bf16, 128>(p, s) : launch_pre_t<bf16, 64>(p, s);
+  return D == 128 ? launch_pre_t<float, 128>(p, s) : launch_pre_t<float, 64>(p, s);
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
+  const long long total = (long long)p.B * p.H * p.ntiles;
+  hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL>), dim3((unsigned)total), dim3(FWD_WAVES * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t s) {
+  const long long total = (long long)p.B * p.H * p.ntiles;
+  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)total), dim3(DKV_WAVES * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, hipStream_t s) {
+  if (dtype == 0) {
+    if (D == 128) return causal ? launch_dq_t<bf16, 128, true>(p, s) : launch_dq_t<bf16, 128, false>(p, s);
+    return causal ? launch_dq_t<bf16, 64, true>(p, s) : launch_dq_t<bf16, 64, false>(p, s);
+  }
+  if (D == 128) return causal ? launch_dq_t<float, 128, true>(p, s) : launch_dq_t<float, 128, false>(p, s);
+  return causal ? launch_dq_t<float, 64, true>(p, s) : launch_dq_t<float, 64, false>(p, s);
+}
+
+hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, hipStream_t s) {
+  if (dtype == 0) {
+    if (D == 128) return causal ? launch_dkdv_t<bf16, 128, true>(p, s) : launch_dkdv_t<bf16, 128, false>(p, s);
+    return causal ? launch_dkdv_t<bf16, 64, true>(p, s) : launch_dkdv_t<bf16, 64, false>(p, s);
+  }
+  if (D == 128) return causal ? launch_dkdv_t<float, 128, true>(p, s) : launch_dkdv_t<float, 128, false>(p, s);
+  return causal ? launch_dkdv_t<float, 64, true>(p, s) : launch_dkdv_t<float, 64, false>(p, s);
+}
+
+}  // namespace fa

@@ -1,0 +1,70 @@
+// Host<->kernel parameter blocks, tile sizes and launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Tile sizes.  Forward and dQ: one workgroup owns FWD_WAVES * 32 queries and
+// walks key tiles of KEY_TILE keys.  dK/dV: one workgroup owns DKV_WAVES * 32
+// keys and walks query tiles of QRY_TILE queries.
+constexpr int FWD_WAVES = 4;
+constexpr int FWD_BM = FWD_WAVES * 32;
+constexpr int KEY_TILE = 64;
+constexpr int DKV_WAVES = 4;
+constexpr int DKV_BN = DKV_WAVES * 32;
+constexpr int QRY_TILE = 32;
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* seg;    // (B, N) or null
+  const int2* qtab;      // per query tile: [first, last] key tile (packed only)
+  int B, H, N, nqt;
+  float scale;           // softmax scale
+  float c;               // scale * log2(e)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* lse2;     // log2-domain LSE (B, H, N)
+  const float* delta;    // D_i = dO_i . O_i (B, H, N)
+  const int32_t* seg;
+  const int2* tab;       // dQ: per query tile key-tile range; dK/dV: per key tile query-tile range
+  int B, H, N, ntiles;
+  float scale, c;
+};
+
+struct PreParams {
+  const void* o;
+  const void* dO;
+  const float* lse;
+  float* delta;
+  float* lse2;
+  long long rows;
+};
+
+// Launchers (defined next to their kernels).  dtype: 0 bf16, 1 fp32.
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, hipStream_t s);
+hipError_t launch_bwd_pre(const PreParams& p, int dtype, int D, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, hipStream_t s);
+// Per-tile range tables from segment ids (see fa_sched.hip).
+hipError_t launch_qtile_table(const int32_t* seg, int B, int N, int tq, int tk, bool causal,
+                              int2* tab, hipStream_t s);
+hipError_t launch_ktile_table(const int32_t* seg, int B, int N, int tk, int tq, bool causal,
+                              int2* tab, hipStream_t s);
+hipError_t launch_seg_check(const int32_t* seg, int B, int N, int32_t* flag, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,146 @@
+"""The C ABI on the host: the library loads, exports what include/fa.h declares,
+and refuses bad arguments with the right status before any HIP call.
+
+No compute runs here (this suite also runs on machines without a GPU); the
+tensor pointers passed are fake, non-null integers that a refusal never touches.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE = 0, 1, 2, 3, 4
+FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_SCALE, FA_ERR_SEG, FA_ERR_HIP, FA_ERR_DEVICE = 5, 6, 7, 8, 9, 10
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import memory_efficient_attention_amd as fa
+    if not os.path.exists(fa.library_path()):
+        fa_build = pytest.importorskip("memory_efficient_attention_amd.build")
+        fa_build.build()
+    return fa.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_status_values_match():
+    text = open(HEADER).read()
+    vals = dict((n, int(v)) for n, v in re.findall(r"\b(FA_\w+)\s*=\s*(\d+)", text))
+    assert vals["FA_OK"] == FA_OK and vals["FA_ERR_DEVICE"] == FA_ERR_DEVICE
+    assert vals["FA_ERR_ALIGN"] == FA_ERR_ALIGN and vals["FA_ERR_SEG"] == FA_ERR_SEG
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared == ["fa_bwd", "fa_check_seg", "fa_fwd", "fa_status_string", "fa_workspace_bytes"]
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r" T (fa_\w+)", out)))
+    assert exported == declared          # and nothing else leaks out of the library
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+GOOD = dict(B=1, H=2, N=64, D=64, dtype=0, scale=0.125)
+P = 0x100000   # fake, 256-aligned, never dereferenced
+
+
+def _fwd(lib, q=P, k=P, v=P, seg=None, scale=0.125, causal=1, o=P, lse=P, B=1, H=2, N=64, D=64,
+         dtype=0, ws=None, ws_bytes=0):
+    return lib.fa_fwd(q, k, v, seg, ctypes.c_float(scale), causal, o, lse, B, H, N, D, dtype, ws,
+                      ws_bytes, None)
+
+
+def _bwd(lib, q=P, k=P, v=P, o=P, do=P, lse=P, seg=None, scale=0.125, causal=1, dq=P, dk=P, dv=P,
+         B=1, H=2, N=64, D=64, dtype=0, ws=P, ws_bytes=1 << 30):
+    return lib.fa_bwd(q, k, v, o, do, lse, seg, ctypes.c_float(scale), causal, dq, dk, dv, B, H, N, D,
+                      dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), FA_ERR_NULL), (dict(lse=None), FA_ERR_NULL), (dict(o=None), FA_ERR_NULL),
+    (dict(B=0), FA_ERR_SHAPE), (dict(H=-1), FA_ERR_SHAPE), (dict(N=0), FA_ERR_SHAPE),
+    (dict(N=(1 << 24) + 1), FA_ERR_SHAPE), (dict(B=1 << 16, H=1 << 10, N=1 << 10), FA_ERR_SHAPE),
+    (dict(D=96), FA_ERR_HEAD_DIM), (dict(D=32), FA_ERR_HEAD_DIM), (dict(D=256), FA_ERR_HEAD_DIM),
+    (dict(dtype=2), FA_ERR_DTYPE), (dict(dtype=-1), FA_ERR_DTYPE),
+    (dict(scale=float("nan")), FA_ERR_SCALE), (dict(scale=float("inf")), FA_ERR_SCALE),
+    (dict(scale=0.0), FA_ERR_SCALE), (dict(scale=-1.0), FA_ERR_SCALE),
+    (dict(q=P + 8), FA_ERR_ALIGN), (dict(v=P + 2), FA_ERR_ALIGN), (dict(lse=P + 2), FA_ERR_ALIGN),
+    (dict(seg=P + 1, ws=P, ws_bytes=1 << 20), FA_ERR_ALIGN),
+    (dict(seg=P), FA_ERR_WORKSPACE), (dict(seg=P, ws=P, ws_bytes=16), FA_ERR_WORKSPACE),
+    (dict(seg=P, ws=P + 16, ws_bytes=1 << 20), FA_ERR_ALIGN),
+])
+def test_fwd_refusals(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(do=None), FA_ERR_NULL), (dict(dv=None), FA_ERR_NULL), (dict(lse=None), FA_ERR_NULL),
+    (dict(N=-5), FA_ERR_SHAPE), (dict(D=80), FA_ERR_HEAD_DIM), (dict(dtype=7), FA_ERR_DTYPE),
+    (dict(scale=float("-inf")), FA_ERR_SCALE), (dict(dk=P + 4), FA_ERR_ALIGN),
+    (dict(ws=None), FA_ERR_WORKSPACE), (dict(ws_bytes=100), FA_ERR_WORKSPACE),
+    (dict(ws=P + 64), FA_ERR_ALIGN),
+])
+def test_bwd_refusals(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_first_failing_check_wins(lib):
+    # a null pointer is reported before a bad shape, a bad shape before a bad dtype
+    assert _fwd(lib, q=None, B=0, dtype=9) == FA_ERR_NULL
+    assert _fwd(lib, B=0, D=96, dtype=9) == FA_ERR_SHAPE
+    assert _fwd(lib, D=96, dtype=9) == FA_ERR_HEAD_DIM
+
+
+def test_workspace_sizes(lib):
+    ws = lib.fa_workspace_bytes
+    assert ws(1, 32, 16384, 128, 0, 0) == 0                    # plain forward needs none
+    assert ws(0, 1, 1, 64, 0, 1) == 0 and ws(1, 1, 1, 96, 0, 1) == 0
+    b1 = ws(1, 32, 8192, 128, 0, 1)
+    b2 = ws(1, 32, 16384, 128, 0, 1)
+    # O(N): two fp32 (B,H,N) arrays plus a 256-byte flag block
+    assert b1 == 256 + 2 * 32 * 8192 * 4 and b2 == 256 + 2 * 32 * 16384 * 4
+    s1 = ws(4, 32, 4096, 128, 1, 1)
+    assert s1 == 256 + 2 * 4 * 32 * 4096 * 4 + 2 * 4 * (4096 // 32) * 8
+    assert ws(1, 1, 100, 64, 1, 0) == 256 + 2 * 256           # tables rounded to 256 B
+    for n in (1000, 2000, 4000):
+        assert ws(1, 8, 2 * n, 64, 1, 1) - 256 <= 2.01 * (ws(1, 8, n, 64, 1, 1) - 256)
+
+
+def test_check_seg(lib):
+    good = np.array([[0, 0, 1, 1, 1, 5], [2, 2, 2, 2, 2, 2]], dtype=np.int32)
+    bad = np.array([[0, 0, 1, 0, 1, 5], [2, 2, 2, 2, 2, 2]], dtype=np.int32)
+    assert lib.fa_check_seg(good.ctypes.data, 2, 6) == FA_OK
+    assert lib.fa_check_seg(bad.ctypes.data, 2, 6) == FA_ERR_SEG
+    # each row is checked on its own: a drop between rows is fine
+    rows = np.array([[0, 1, 2], [0, 0, 1]], dtype=np.int32)
+    assert lib.fa_check_seg(rows.ctypes.data, 2, 3) == FA_OK
+    assert lib.fa_check_seg(None, 2, 3) == FA_ERR_NULL
+    assert lib.fa_check_seg(rows.ctypes.data, 0, 3) == FA_ERR_SHAPE
+
+
+def test_python_check_seg_raises():
+    import memory_efficient_attention_amd as fa
+    fa.fa_check_seg(np.zeros((1, 5), np.int32))
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_check_seg(np.array([[1, 0]], np.int32))
+    assert e.value.status == FA_ERR_SEG
+
+
+def test_status_strings(lib):
+    seen = set()
+    for s in range(0, 11):
+        txt = lib.fa_status_string(s).decode()
+        assert txt and txt != "unknown status"
+        seen.add(txt)
+    assert len(seen) == 11
+    assert lib.fa_status_string(1234).decode() == "unknown status"

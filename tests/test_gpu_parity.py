@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
+
+Bounds, per tensor:
+* bf16 inputs: |O - O_ref| <= max(1e-2, one bf16 ulp of O_ref) element-wise
+  (1e-2 is the stated bound; the ulp allowance covers the bf16 rounding of
+  the output itself, which alone can exceed 1e-2 where |O| >= 2), and
+  relative L2 error <= 2e-2 for dQ, dK and dV;
+* fp32 inputs: O max-abs <= 1e-4 and relative L2 <= 1e-4;
+* LSE max-abs <= 1e-3 (bf16) / 1e-5 (fp32).
+
+Small shapes run the whole oracle; they span several tiles and a ragged tail
+(N = 1, 17, 129, 255, 257, 300) in every masking mode.  The five workloads
+run at full size on the GPU; the oracle then checks whole sampled heads,
+sampled rows, or (for very long packed rows) whole segments run alone, which
+equals the packed row by the oracle's own pinned invariant.  Full-size outputs
+are also checked against identities that need no oracle.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import (check_grad, check_lse, check_o, down, run_gpu, say, upload,
+                         upload_seg)
+from oracle import attention_backward, attention_forward, attention_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import memory_efficient_attention_amd as fa
+    fa.load_library()        # raises if the HIP library is missing: no fallback
+    torch.manual_seed(0)
+    yield
+
+
+def _oracle_full(t, seg, scale, causal):
+    o, lse = attention_forward(t["q"], t["k"], t["v"], seg, scale, causal)
+    dq, dk, dv = attention_backward(t["q"], t["k"], t["v"], t["do"], seg, scale, causal, o=o, lse=lse)
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+
+
+def _compare(out, ref, dtype, sl=(slice(None),), tag=""):
+    """Compare GPU outputs (device tensors) against oracle arrays on index `sl`."""
+    o = down(out["o"][sl])
+    check_o(o, ref["o"], dtype, f"O{tag}")
+    check_lse(down(out["lse"][sl]), ref["lse"], dtype)
+    errs = [check_grad(down(out[n][sl]), ref[n], dtype, f"{n}{tag}") for n in ("dq", "dk", "dv")]
+    return errs
+
+
+# ---------------------------------------------------------------- small shapes
+
+SHAPES = [(1, 2, 1, 64), (1, 1, 17, 64), (2, 2, 255, 128), (1, 2, 257, 64), (1, 3, 300, 128),
+          (2, 1, 129, 128)]
+MODES = {"causal": (False, True), "packed": (True, True), "packed_bidir": (True, False),
+         "full": (False, False)}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,H,N,D", SHAPES)
+def test_small_shapes(B, H, N, D, dtype, mode):
+    packed, causal = MODES[mode]
+    seed = 1000 + 7 * N + D + B
+    say(f"small case B{B} H{H} N{N} D{D} {dtype} {mode} seed {seed}")
+    t = workloads.make_tensors(B, H, N, D, dtype, seed)
+    seg = workloads.random_segments(B, N, seed, max_len=max(1, N // 4)) if packed else None
+    scale = 1.0 / np.sqrt(D)
+    out = run_gpu(t, seg, dtype, scale, causal)
+    ref = _oracle_full(t, seg, scale, causal)
+    _compare(out, ref, dtype)
+
+
+def test_short_segments_many_tiles():
+    """Segments of 1..5 tokens: nearly every tile pair is cross-segment."""
+    B, H, N, D = 2, 2, 700, 128
+    say("short segments B2 H2 N700 D128 bf16")
+    t = workloads.make_tensors(B, H, N, D, "bf16", 77)
+    seg = workloads.random_segments(B, N, 77, max_len=5)
+    for causal in (True, False):
+        out = run_gpu(t, seg, "bf16", 0.09, causal)
+        _compare(out, _oracle_full(t, seg, 0.09, causal), "bf16")
+
+
+def test_segment_ids_need_not_start_at_zero():
+    """Ids are compared for equality only; any non-decreasing ids work."""
+    B, H, N, D = 1, 2, 200, 64
+    say("offset segment ids B1 H2 N200 D64")
+    t = workloads.make_tensors(B, H, N, D, "bf16", 78)
+    seg = workloads.random_segments(B, N, 78, max_len=50) * 3 + 1000
+    out = run_gpu(t, seg, "bf16", 0.125, True)
+    _compare(out, _oracle_full(t, seg, 0.125, True), "bf16")
+
+
+# ---------------------------------------------------------------- the workloads
+
+def test_tiny_fp32_one_segment():
+    w = workloads.get("tiny_causal_fp32")
+    say(f"workload {w.name}: {w.note}")
+    t = w.tensors()
+    seg = w.seg()
+    ref = _oracle_full(t, seg, w.scale, True)
+    out = run_gpu(t, seg, w.dtype, w.scale, True)
+    _compare(out, ref, w.dtype)
+    plain = run_gpu(t, None, w.dtype, w.scale, True)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert bool((out[n] == plain[n]).all()), f"{n}: one-segment packed != causal"
+
+
+def test_causal_2k_full_oracle():
+    w = workloads.get("causal_2k")
+    say(f"workload {w.name}: {w.note}")
+    t = w.tensors()
+    out = run_gpu(t, None, w.dtype, w.scale, True)
+    ref = _oracle_full(t, None, w.scale, True)
+    errs = _compare(out, ref, w.dtype)
+    say(f"  rel-L2 dq/dk/dv {errs}")
+    again = run_gpu(t, None, w.dtype, w.scale, True)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert bool((out[n] == again[n]).all()), f"{n} differs between identical runs"
+
+
+def _seg_sums(x, seg):
+    """Per-segment sums over tokens of x (B,H,N,D), and of |x|, in fp64."""
+    import torch
+    B, H, N, D = x.shape
+    xs = x.to(torch.float64)
+    ids = torch.zeros((B, N), dtype=torch.int64, device=x.device) if seg is None else seg.to(torch.int64)
+    ids = ids - ids[:, :1]
+    nseg = int(ids.max().item()) + 1
+    sums = torch.zeros((B, H, nseg, D), dtype=torch.float64, device=x.device)
+    mags = torch.zeros_like(sums)
+    for b in range(B):
+        sums[b].index_add_(1, ids[b], xs[b])
+        mags[b].index_add_(1, ids[b], xs[b].abs())
+    return sums, mags
+
+
+def _invariants(out, tol=1e-2):
+    """Identities of exact attention that hold at any size (no oracle):
+    per segment sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i; per head
+    sum_i q_i . dQ_i = sum_j k_j . dK_j."""
+    seg = out["seg"]
+    dk_s, dk_m = _seg_sums(out["dk"], seg)
+    assert bool((dk_s.abs() <= tol * dk_m + 1e-6).all()), \
+        f"sum dK per segment: worst {(dk_s.abs() / (dk_m + 1e-30)).max().item():.3e}"
+    dv_s, dv_m = _seg_sums(out["dv"], seg)
+    do_s, _ = _seg_sums(out["do"], seg)
+    assert bool(((dv_s - do_s).abs() <= tol * dv_m + 1e-6).all()), "sum dV != sum dO per segment"
+    lhs = (out["q"].double() * out["dq"].double()).sum(dim=(2, 3))
+    rhs = (out["k"].double() * out["dk"].double()).sum(dim=(2, 3))
+    mag = (out["q"].double() * out["dq"].double()).abs().sum(dim=(2, 3))
+    assert bool(((lhs - rhs).abs() <= tol * mag).all()), "sum q.dQ != sum k.dK"
+
+
+def test_packed_short_examples_4k():
+    w = workloads.get("packed_short_4k")
+    say(f"workload {w.name}: {w.note}")
+    t = w.tensors()
+    seg = w.seg()
+    out = run_gpu(t, seg, w.dtype, w.scale, True)
+    for b, h in [(0, 0), (1, 17), (3, 31)]:
+        say(f"  oracle head b{b} h{h}")
+        tb = {n: t[n][b:b + 1, h:h + 1] for n in t}
+        ref = _oracle_full(tb, seg[b:b + 1], w.scale, True)
+        _compare(out, ref, w.dtype, (slice(b, b + 1), slice(h, h + 1)), f"[b{b} h{h}]")
+    _invariants(out)
+
+
+def test_causal_16k():
+    w = workloads.get("causal_16k")
+    say(f"workload {w.name}: {w.note}")
+    t = w.tensors()
+    out = run_gpu(t, None, w.dtype, w.scale, True)
+    b, h = 0, 5
+    say(f"  oracle head b{b} h{h}")
+    tb = {n: t[n][b:b + 1, h:h + 1] for n in t}
+    ref = _oracle_full(tb, None, w.scale, True)
+    _compare(out, ref, w.dtype, (slice(b, b + 1), slice(h, h + 1)), f"[b{b} h{h}]")
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 16383], rng.integers(0, w.N, 27)]))
+    o_all, lse_all = down(out["o"]), down(out["lse"])
+    for hh in range(w.H):
+        o_r, l_r = attention_rows(t["q"][0, hh], t["k"][0, hh], t["v"][0, hh], rows, None, w.scale, True)
+        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}")
+        check_lse(lse_all[0, hh, rows], l_r, w.dtype)
+    _invariants(out)
+
+
+def test_single_segment_8k_bitwise_equals_causal():
+    w = workloads.get("single_segment_8k")
+    say(f"workload {w.name}: {w.note}")
+    t = w.tensors()
+    packed = run_gpu(t, w.seg(), w.dtype, w.scale, True)
+    causal = run_gpu(t, None, w.dtype, w.scale, True)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert bool((packed[n] == causal[n]).all()), f"{n}: single-segment packed != causal"
+    rows = np.array([0, 5, 100, 4097, 8191])
+    o_r, l_r = attention_rows(t["q"][0, 3], t["k"][0, 3], t["v"][0, 3], rows, None, w.scale, True)
+    check_o(down(packed["o"][0, 3, rows]), o_r, w.dtype)
+    check_lse(down(packed["lse"][0, 3, rows]), l_r, w.dtype)
+
+
+def test_packed_long_documents_64k():
+    w = workloads.get("packed_long_64k")
+    say(f"workload {w.name}: {w.note}")
+    t = w.tensors()
+    seg = w.seg()
+    out = run_gpu(t, seg, w.dtype, w.scale, True)
+    lens = workloads.segment_lengths(seg[0])
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    o_all, lse_all = down(out["o"]), down(out["lse"])
+    rng = np.random.default_rng(5)
+    # sampled rows of every head against the full-row oracle (explicit mask over all keys)
+    for hh in range(w.H):
+        rows = np.unique(np.concatenate([starts, starts + 1, rng.integers(0, w.N, 12), [w.N - 1]]))
+        rows = rows[rows < w.N]
+        o_r, l_r = attention_rows(t["q"][0, hh], t["k"][0, hh], t["v"][0, hh], rows, seg[0], w.scale, True)
+        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}")
+        check_lse(lse_all[0, hh, rows], l_r, w.dtype)
+    # whole segments: a packed row equals each segment run alone
+    order = np.argsort(lens)
+    for si, hh in [(order[0], 0), (order[1], 7), (len(lens) - 1, 3)]:
+        s0, L = int(starts[si]), int(lens[si])
+        say(f"  oracle segment {si} [{s0}, {s0 + L}) head {hh}")
+        tb = {n: t[n][:, hh:hh + 1, s0:s0 + L] for n in t}
+        ref = _oracle_full(tb, None, w.scale, True)
+        _compare(out, ref, w.dtype, (slice(0, 1), slice(hh, hh + 1), slice(s0, s0 + L)), f"[seg {si} h{hh}]")
+    _invariants(out)
+
+
+def test_packed_outputs_do_not_depend_on_other_segments():
+    """Changing one segment's inputs leaves every other segment's results bit-identical."""
+    import torch
+    B, H, N, D = 1, 2, 1000, 128
+    say("segment isolation B1 H2 N1000 D128")
+    t = workloads.make_tensors(B, H, N, D, "bf16", 91)
+    seg = workloads.random_segments(B, N, 91, max_len=300)
+    a = run_gpu(t, seg, "bf16", 0.088, True)
+    lens = workloads.segment_lengths(seg[0])
+    s0, L = sum(lens[:1]), lens[1]
+    t2 = {n: x.copy() for n, x in t.items()}
+    for n in t2:
+        t2[n][:, :, s0:s0 + L] = workloads.make_tensors(B, H, L, D, "bf16", 92)[n]
+    b2 = run_gpu(t2, seg, "bf16", 0.088, True)
+    keep = torch.ones(N, dtype=torch.bool, device="cuda")
+    keep[s0:s0 + L] = False
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        x, y = a[n][:, :, keep], b2[n][:, :, keep]
+        assert bool((x == y).all()), f"{n} of other segments changed"
