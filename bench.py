@@ -1,0 +1,402 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path: one step = fa_fwd + fa_bwd over one batch.
+
+Prints ONE JSON line: effective TFLOP/s of forward + backward counting only
+visible (unmasked) flops, 14 * D * V for V visible (query, key) pairs (4DV in
+the forward's two products, 10DV in the backward's five), and its share of the
+MI355X dense bf16 MFMA peak (2.5 PFLOP/s).  Inputs are seeded synthetic
+tensors already resident in HBM when the timed region starts.
+
+Beside the headline number the line carries
+* ``roofline``: the dominant kernel's algorithmic flops per launch over its
+  average launch time, measured with HIP events recorded on the launch stream
+  around that kernel in every timed step; ``traffic`` is its HBM bytes per
+  launch from rocprofv3 counters (profiles/traffic.json), or null when the
+  kernel sources changed since the counters were taken;
+* ``cpu_baseline``: the fp64 oracle timed on this host on a bounded sample of
+  the same workload (the last 4096 query rows of one head).
+
+Other modes: ``--all`` prints a table over every workload (and the causal
+comparator of each packed one); ``--copy-calibration`` runs a plain
+elementwise copy of known size (the reference for HBM byte counters);
+``--ingest-counters`` turns rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
+script into profiles/traffic.json.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s fwd+bwd (visible FLOPs) and % bf16 MFMA peak, N=8k/16k d=128"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "causal_16k"
+KERNELS = ("fwd", "pre", "dkdv", "dq")
+KERNEL_NAMES = {"fwd": "fwd_kernel", "pre": "bwd_pre_kernel", "dkdv": "dkdv_kernel", "dq": "dq_kernel"}
+
+
+# ---------------------------------------------------------------- helpers
+
+def visible_pairs(B, H, N, seg, causal=True) -> int:
+    """Visible (query, key) pairs over all (batch, head): sum of L(L+1)/2 per segment."""
+    import workloads
+    per_row = []
+    for b in range(B):
+        lens = [N] if seg is None else workloads.segment_lengths(seg[b])
+        per_row.append(sum(L * (L + 1) // 2 if causal else L * L for L in lens))
+    return H * sum(per_row)
+
+
+def kernel_sources_sha() -> str:
+    d = os.path.join(ROOT, "memory_efficient_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        import torch
+        self.hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        vp = ctypes.c_void_p
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        self.hip.hipEventRecord.argtypes = [vp, vp]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self.hip.hipEventDestroy.argtypes = [vp]
+        self.made = []
+
+    def new(self) -> int:
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.made.append(e.value)
+        return e.value
+
+    def record(self, e: int, stream: int) -> None:
+        if self.hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
+
+
+def alg_flops(kernel: str, D: int, V: int) -> float:
+    """Algorithmic (visible-pair) flops of one launch of each kernel."""
+    return {"fwd": 4.0, "dkdv": 8.0, "dq": 6.0, "pre": 0.0}[kernel] * D * V
+
+
+def pre_bytes(B, H, N, D, elt) -> float:
+    # reads O, dO, LSE; writes D_i and the log2 LSE
+    return 2.0 * B * H * N * D * elt + 3.0 * B * H * N * 4
+
+
+# ---------------------------------------------------------------- one workload
+
+def run_workload(w, steps: int, warmup: int, seg_override="keep", causal=True, quiet=False):
+    import numpy as np
+    import torch
+
+    import memory_efficient_attention_amd as fa
+
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t_np = w.tensors()
+    x = {n: torch.from_numpy(a).to(dev).to(tdt) for n, a in t_np.items()}
+    seg_np = w.seg() if seg_override == "keep" else seg_override
+    seg = None if seg_np is None else torch.from_numpy(seg_np).to(dev)
+    B, H, N, D = w.B, w.H, w.N, w.D
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
+    ws_f = torch.empty(max(fa.fa_workspace_bytes(B, H, N, D, seg is not None, False), 256),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(fa.fa_workspace_bytes(B, H, N, D, seg is not None, True), dtype=torch.uint8,
+                       device=dev)
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(evs=None):
+        if evs:
+            ev.record(evs[0], stream)
+        fa.fa_fwd(x["q"], x["k"], x["v"], seg, w.scale, causal, out=o, lse=lse, workspace=ws_f)
+        if evs:
+            ev.record(evs[1], stream)
+        fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, seg, w.scale, causal, dq=dq, dk=dk, dv=dv,
+                  workspace=ws_b, events=evs[2:6] if evs else None)
+
+    for _ in range(warmup):
+        step()
+    stage_ev = [[ev.new() for _ in range(6)] for _ in range(steps)]
+    t0, t1 = ev.new(), ev.new()
+    torch.cuda.synchronize()
+    ev.record(t0, stream)
+    for i in range(steps):
+        step(stage_ev[i])
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    total_ms = ev.ms(t0, t1)
+    stage = {k: 0.0 for k in KERNELS}
+    for e in stage_ev:
+        stage["fwd"] += ev.ms(e[0], e[1])
+        stage["pre"] += ev.ms(e[2], e[3])
+        stage["dkdv"] += ev.ms(e[3], e[4])
+        stage["dq"] += ev.ms(e[4], e[5])
+    stage = {k: v / steps for k, v in stage.items()}
+    ev.close()
+    ms = total_ms / steps
+    V = visible_pairs(B, H, N, seg_np, causal)
+    flops = 14.0 * D * V
+    res = dict(ms=ms, V=V, flops=flops, tflops=flops / (ms * 1e-3) / 1e12, stage_ms=stage,
+               t_np=t_np, seg_np=seg_np)
+    del x, o, lse, dq, dk, dv, ws_f, ws_b
+    torch.cuda.empty_cache()
+    return res
+
+
+CPU_SAMPLE_ROWS = 4096
+
+
+def cpu_baseline(w, t_np, seg_np, causal=True):
+    """The fp64 oracle on a bounded sample of the workload, on this host's cores.
+
+    Sample: the last CPU_SAMPLE_ROWS query rows of (batch 0, head 0), forward
+    (O, LSE) and backward (dQ of those rows and their dK, dV contributions),
+    each with the explicit mask over all N keys.  Credited flops are 14 * D
+    times the visible pairs of those rows."""
+    import numpy as np
+
+    from oracle import attention_backward_rows, attention_rows, visible_mask
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    b, h = 0, 0
+    R = min(CPU_SAMPLE_ROWS, w.N)
+    rows = np.arange(w.N - R, w.N)
+    s = {n: a[b, h] for n, a in t_np.items()}
+    seg_row = None if seg_np is None else seg_np[b]
+    t0 = time.perf_counter()
+    o_r, lse_r = attention_rows(s["q"], s["k"], s["v"], rows, seg_row, w.scale, causal)
+    attention_backward_rows(s["q"], s["k"], s["v"], s["do"], o_r, lse_r, rows, seg_row, w.scale, causal)
+    el = time.perf_counter() - t0
+    V = int(visible_mask(rows, w.N, seg_row, causal).sum())
+    return {"value": round(14.0 * w.D * V / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"query rows [{w.N - R}, {w.N}) of (batch 0, head 0), N={w.N}, D={w.D}: fp64 "
+                      f"forward + backward with the explicit mask over all keys ({V} visible pairs, "
+                      f"{el:.1f} s); cores = BLAS threads",
+            "seconds": round(el, 2)}
+
+
+def roofline(w, res):
+    stage = res["stage_ms"]
+    dom = max(("fwd", "dkdv", "dq"), key=lambda k: stage[k])
+    avg_ms = stage[dom]
+    alg = alg_flops(dom, w.D, res["V"])
+    achieved = alg / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    traffic = None
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(path):
+        try:
+            with open(path) as f:
+                rec = json.load(f).get(w.name, {}).get(dom)
+            if rec and rec.get("source_sha") == kernel_sources_sha():
+                traffic = rec["bytes_per_launch"]
+        except (OSError, ValueError, KeyError):
+            traffic = None
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": KERNEL_NAMES[dom],
+            "avg_ms": round(avg_ms, 4), "alg_flops_per_launch": alg}
+
+
+# ---------------------------------------------------------------- modes
+
+def headline(args):
+    import workloads
+    w = workloads.get(args.workload)
+    res = run_workload(w, args.steps, args.warmup)
+    out = {
+        "metric": METRIC,
+        "value": round(res["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q, k, v, dO)",
+        "config": {"workload": f"{w.name}: {w.note}", "global_batch": w.B, "seq_len": w.N,
+                   "heads": w.H, "head_dim": w.D, "causal": True,
+                   "segments": "none" if w.layout == "none" else w.layout,
+                   "visible_pairs": res["V"], "visible_flops": res["flops"]},
+        "pct_bf16_peak": round(100.0 * res["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {k: round(v, 4) for k, v in res["stage_ms"].items()},
+        "roofline": roofline(w, res),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, res["t_np"], res["seg_np"])
+    print(json.dumps(out), flush=True)
+
+
+def report_all(args):
+    import workloads
+    rows = []
+    names = ["tiny_causal_fp32", "causal_2k", "packed_short_4k", "single_segment_8k", "causal_16k",
+             "packed_long_64k"]
+    for name in names:
+        w = workloads.get(name)
+        print(f"# running {name}", file=sys.stderr, flush=True)
+        r = run_workload(w, args.steps, args.warmup)
+        row = dict(workload=name, ms=r["ms"], tflops=r["tflops"], V=r["V"], stages=r["stage_ms"])
+        if w.layout in ("short", "long", "single"):
+            c = run_workload(w, args.steps, args.warmup, seg_override=None)
+            row["causal_ms"] = c["ms"]
+            row["causal_V"] = c["V"]
+            row["speedup_vs_causal"] = c["ms"] / r["ms"]
+            row["visible_ratio"] = c["V"] / r["V"]
+        rows.append(row)
+        print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()}),
+              flush=True)
+    print("\n| workload | ms fwd+bwd | fwd | pre | dK/dV | dQ | eff. TFLOP/s | % peak | packed speedup vs causal (visible ratio) |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        s = r["stages"]
+        sp = (f"{r['speedup_vs_causal']:.2f}x ({r['visible_ratio']:.2f}x)" if "speedup_vs_causal" in r else "")
+        print(f"| {r['workload']} | {r['ms']:.3f} | {s['fwd']:.3f} | {s['pre']:.3f} | {s['dkdv']:.3f} | "
+              f"{s['dq']:.3f} | {r['tflops']:.1f} | {100 * r['tflops'] / PEAK_BF16_TFLOPS:.1f} | {sp} |")
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A plain copy of COPY_BYTES (read once, written once): torch.neg into a
+    second buffer, timed by the counters, not by us."""
+    import torch
+    n = COPY_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "kernel": "neg"}), flush=True)
+
+
+def _counter_rows(path):
+    """(kernel name, counter name, value) rows of rocprofv3 counter CSVs under path."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r.get("Kernel_Name", ""), r.get("Counter_Name", ""),
+                             float(r.get("Counter_Value", "nan"))))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    return rows
+
+
+def _avg(rows, counter, match):
+    vals = [v for k, c, v in rows if c == counter and match in k]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {match!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def ingest_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload):
+    """profiles/traffic.json entry: HBM bytes per launch of each attention
+    kernel = counter (KiB per dispatch) scaled so that the plain copy reads
+    and writes exactly COPY_BYTES."""
+    f_rows, w_rows = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    cf, _ = _avg(_counter_rows(cal_fetch_dir), "FETCH_SIZE", "neg")
+    cw, _ = _avg(_counter_rows(cal_write_dir), "WRITE_SIZE", "neg")
+    kf, kw = COPY_BYTES / cf, COPY_BYTES / cw          # bytes per counter unit
+    entry = {}
+    for short, name in KERNEL_NAMES.items():
+        try:
+            fv, n = _avg(f_rows, "FETCH_SIZE", name)
+            wv, _ = _avg(w_rows, "WRITE_SIZE", name)
+        except SystemExit:
+            continue
+        entry[short] = {"kernel": name, "dispatches": n, "fetch_bytes": fv * kf, "write_bytes": wv * kw,
+                        "bytes_per_launch": fv * kf + wv * kw, "source_sha": kernel_sources_sha()}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            data = json.load(fh)
+    data[workload] = entry
+    data["_calibration"] = {"copy_bytes": COPY_BYTES, "fetch_counter_per_copy": cf,
+                            "write_counter_per_copy": cw, "bytes_per_fetch_unit": kf,
+                            "bytes_per_write_unit": kw}
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps(entry, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="table over every workload instead of the JSON line")
+    ap.add_argument("--copy-calibration", action="store_true", help="plain copy of known size for counters")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
+                                                           "CAL_WRITE_DIR"),
+                    help="write profiles/traffic.json from rocprofv3 counter runs (CPU only)")
+    args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, args.workload)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this attention path runs on one GPU (one process, one device); runs on more "
+              "than one GPU are not part of it.  How it would shard across GPUs (by batch and head, "
+              "no exchange) is described in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+    elif args.all:
+        report_all(args)
+    else:
+        headline(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -116,6 +116,22 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fa_bwd with per-stage HIP events, for profiling callers that need the time
+ * of each backward kernel on its own stream.  `events` is NULL (then this is
+ * fa_bwd) or points to 4 hipEvent_t handles, each may be NULL, created by the
+ * caller on the current device.  They are recorded on `stream`: events[0]
+ * before the D_i preprocess kernel, events[1] before the dK/dV kernel,
+ * events[2] before the dQ kernel, events[3] after it.  Any segment schedule
+ * kernels run before events[0].  Same arguments and errors as fa_bwd, plus
+ * FA_ERR_HIP if recording an event fails.
+ */
+fa_status fa_bwd_timed(const void* q, const void* k, const void* v, const void* o,
+                       const void* dO, const float* lse, const int32_t* seg,
+                       float scale, int causal, void* dq, void* dk, void* dv,
+                       int B, int H, int N, int D, fa_dtype dtype,
+                       void* ws, size_t ws_bytes, void* stream, void* const* events);
+
+/*
  * Host-side precondition check of a HOST copy of seg: FA_OK when every row is
  * non-decreasing, FA_ERR_SEG otherwise, FA_ERR_NULL / FA_ERR_SHAPE for bad
  * arguments.  Makes no HIP call.

@@ -48,6 +48,11 @@ def load_library():
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
                            "`python -m memory_efficient_attention_amd.build`")
+    # torch first: its bundled HIP runtime (SONAME libamdhip64.so.7) must be the
+    # one in the process, so that libfa.so binds to it and streams/pointers
+    # from torch are valid in the library.  Loaded the other way round, torch
+    # would map a second runtime.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -56,6 +61,8 @@ def load_library():
     lib.fa_fwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, vp, sz, vp, vp]
+    lib.fa_bwd_timed.restype = i
     lib.fa_check_seg.argtypes = [vp, i, i]
     lib.fa_check_seg.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -143,8 +150,11 @@ def fa_fwd(q, k, v, seg=None, scale=None, causal=True, out=None, lse=None, works
 
 
 def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=None, dv=None,
-           workspace=None):
-    """Backward pass from dO; returns (dq, dk, dv)."""
+           workspace=None, events=None):
+    """Backward pass from dO; returns (dq, dk, dv).
+
+    ``events``: optional sequence of 4 raw hipEvent_t handles (ints or None)
+    recorded between the backward kernels (fa_bwd_timed in the C ABI)."""
     import torch
     B, H, N, D = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
@@ -162,10 +172,15 @@ def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=N
     ws = workspace
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                    lse.data_ptr(), seg_p, ctypes.c_float(scale), int(bool(causal)),
-                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, _dtype_code(q),
-                    ws.data_ptr(), nbytes, _stream())
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+            lse.data_ptr(), seg_p, ctypes.c_float(scale), int(bool(causal)),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, _dtype_code(q),
+            ws.data_ptr(), nbytes, _stream())
+    if events is None:
+        st = lib.fa_bwd(*args)
+    else:
+        ev = (ctypes.c_void_p * 4)(*[e or None for e in events])
+        st = lib.fa_bwd_timed(*args, ev)
     if st:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv

@@ -145,10 +145,17 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   return FA_OK;
 }
 
-FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                        const float* lse, const int32_t* seg, float scale, int causal, void* dq, void* dk,
-                        void* dv, int B, int H, int N, int D, fa_dtype dtype, void* ws, size_t ws_bytes,
-                        void* stream) {
+namespace {
+
+bool record(void* const* events, int i, hipStream_t s) {
+  if (!events || !events[i]) return true;
+  return hipEventRecord((hipEvent_t)events[i], s) == hipSuccess;
+}
+
+fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, const int32_t* seg, float scale, int causal, void* dq, void* dk,
+                   void* dv, int B, int H, int N, int D, fa_dtype dtype, void* ws, size_t ws_bytes,
+                   void* stream, void* const* events) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   if (fa_status st = common_checks(B, H, N, D, dtype, scale)) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
@@ -176,6 +183,7 @@ FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void*
       return FA_ERR_HIP;
   }
 
+  if (!record(events, 0, s)) return FA_ERR_HIP;
   fa::PreParams pp{};
   pp.o = o;
   pp.dO = dO;
@@ -202,14 +210,35 @@ FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void*
   p.scale = scale;
   p.c = log2e_scale(scale);
 
+  if (!record(events, 1, s)) return FA_ERR_HIP;
   p.tab = seg ? (const int2*)(w + L.ktab) : nullptr;
   p.ntiles = (N + fa::DKV_BN - 1) / fa::DKV_BN;
   if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, s) != hipSuccess) return FA_ERR_HIP;
 
+  if (!record(events, 2, s)) return FA_ERR_HIP;
   p.tab = seg ? (const int2*)(w + L.qtab) : nullptr;
   p.ntiles = (N + fa::FWD_BM - 1) / fa::FWD_BM;
   if (fa::launch_bwd_dq(p, dt, D, causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  if (!record(events, 3, s)) return FA_ERR_HIP;
   return FA_OK;
+}
+
+}  // namespace
+
+FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                        const float* lse, const int32_t* seg, float scale, int causal, void* dq, void* dk,
+                        void* dv, int B, int H, int N, int D, fa_dtype dtype, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return bwd_impl(q, k, v, o, dO, lse, seg, scale, causal, dq, dk, dv, B, H, N, D, dtype, ws, ws_bytes,
+                  stream, nullptr);
+}
+
+FA_API fa_status fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                              const float* lse, const int32_t* seg, float scale, int causal, void* dq,
+                              void* dk, void* dv, int B, int H, int N, int D, fa_dtype dtype, void* ws,
+                              size_t ws_bytes, void* stream, void* const* events) {
+  return bwd_impl(q, k, v, o, dO, lse, seg, scale, causal, dq, dk, dv, B, H, N, D, dtype, ws, ws_bytes,
+                  stream, events);
 }
 
 FA_API fa_status fa_check_seg(const int32_t* host_seg, int B, int N) {

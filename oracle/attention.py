@@ -39,7 +39,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["visible_mask", "attention_forward", "attention_backward",
-           "attention_rows", "visible_pairs"]
+           "attention_rows", "attention_backward_rows", "visible_pairs"]
 
 
 def visible_mask(rows: np.ndarray, N: int, seg_row: np.ndarray | None,
@@ -147,6 +147,33 @@ def attention_rows(q_bh, k_bh, v_bh, rows, seg_row=None, scale=None, causal=True
     l = _row_lse(s)
     p = np.exp(s - l[:, None])
     return p @ v_bh, l
+
+
+def attention_backward_rows(q_bh, k_bh, v_bh, do_bh, o_rows, lse_rows, rows, seg_row=None,
+                            scale=None, causal=True):
+    """The backward restricted to selected query rows of one (batch, head).
+
+    Returns dQ of those rows and the contributions those rows make to dK and
+    dV (full (N, D) arrays); summed over a partition of all rows they give
+    attention_backward's dK and dV.  ``o_rows``/``lse_rows`` are the rows' O
+    and LSE from attention_rows.
+    """
+    q_bh = np.asarray(q_bh, dtype=np.float64)
+    k_bh = np.asarray(k_bh, dtype=np.float64)
+    v_bh = np.asarray(v_bh, dtype=np.float64)
+    do_bh = np.asarray(do_bh, dtype=np.float64)
+    N, D = k_bh.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    scale = float(scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    mask = visible_mask(rows, N, seg_row, causal)
+    s = _scores(q_bh[rows], k_bh, scale, mask)
+    p = np.exp(s - np.asarray(lse_rows, dtype=np.float64)[:, None])
+    dp = do_bh[rows] @ v_bh.T
+    dr = np.sum(do_bh[rows] * np.asarray(o_rows, dtype=np.float64), axis=1)
+    ds = p * (dp - dr[:, None])
+    return scale * (ds @ k_bh), scale * (ds.T @ q_bh[rows]), p.T @ do_bh[rows]
 
 
 def visible_pairs(N: int, seg_row: np.ndarray | None, causal: bool = True) -> int:

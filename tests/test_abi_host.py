@@ -42,7 +42,8 @@ def test_header_status_values_match():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
-    assert declared == ["fa_bwd", "fa_check_seg", "fa_fwd", "fa_status_string", "fa_workspace_bytes"]
+    assert declared == ["fa_bwd", "fa_bwd_timed", "fa_check_seg", "fa_fwd", "fa_status_string",
+                        "fa_workspace_bytes"]
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = sorted(set(re.findall(r" T (fa_\w+)", out)))
     assert exported == declared          # and nothing else leaks out of the library

@@ -140,13 +140,19 @@ def _seg_sums(x, seg):
     return sums, mags
 
 
-def _invariants(out, tol=1e-2):
+def _invariants(out, tol=1e-2, tol_dk=0.1):
     """Identities of exact attention that hold at any size (no oracle):
     per segment sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i; per head
-    sum_i q_i . dQ_i = sum_j k_j . dK_j."""
+    sum_i q_i . dQ_i = sum_j k_j . dK_j.
+
+    Bounds are relative to the sum of magnitudes.  sum dK = 0 rests on each
+    row of dS summing to zero; with dS rounded to bf16 and D_i taken from the
+    bf16-stored O, a row sums to O(2^-9 |D_i|) instead, which on segments of a
+    few tokens reaches a few percent of sum |dK|; tol_dk = 0.1 still fails any
+    structural error (a missed or extra tile), which gives ratios of order 1."""
     seg = out["seg"]
     dk_s, dk_m = _seg_sums(out["dk"], seg)
-    assert bool((dk_s.abs() <= tol * dk_m + 1e-6).all()), \
+    assert bool((dk_s.abs() <= tol_dk * dk_m + 1e-6).all()), \
         f"sum dK per segment: worst {(dk_s.abs() / (dk_m + 1e-30)).max().item():.3e}"
     dv_s, dv_m = _seg_sums(out["dv"], seg)
     do_s, _ = _seg_sums(out["do"], seg)

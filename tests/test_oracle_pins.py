@@ -14,8 +14,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (attention_backward, attention_forward, attention_rows,
-                    visible_mask, visible_pairs)
+from oracle import (attention_backward, attention_backward_rows, attention_forward,
+                    attention_rows, visible_mask, visible_pairs)
 import workloads
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_n3_d1.json")
@@ -214,6 +214,26 @@ def test_rows_helper_matches_forward():
     o_r, lse_r = attention_rows(q[0, 0], k[0, 0], v[0, 0], rows, seg[0], 0.3, True)
     np.testing.assert_allclose(o_r, o[0, 0, rows], rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(lse_r, lse[0, 0, rows], rtol=1e-14, atol=1e-14)
+
+
+def test_backward_rows_partition_sums_to_full():
+    """dQ rows and the per-row-block dK/dV contributions add up to the full backward."""
+    B, H, N, D = 1, 1, 45, 8
+    q, k, v, do = (_rand((B, H, N, D), 85 + s) for s in range(4))
+    seg = workloads.random_segments(B, N, 85, max_len=20)
+    for causal in (True, False):
+        o, lse = attention_forward(q, k, v, seg, 0.3, causal)
+        dq, dk, dv = attention_backward(q, k, v, do, seg, 0.3, causal)
+        dk_sum, dv_sum = np.zeros((N, D)), np.zeros((N, D))
+        for rows in (np.arange(0, 10), np.arange(10, 31), np.arange(31, 45)):
+            o_r, l_r = attention_rows(q[0, 0], k[0, 0], v[0, 0], rows, seg[0], 0.3, causal)
+            dq_r, dk_r, dv_r = attention_backward_rows(q[0, 0], k[0, 0], v[0, 0], do[0, 0], o_r, l_r,
+                                                       rows, seg[0], 0.3, causal)
+            np.testing.assert_allclose(dq_r, dq[0, 0, rows], rtol=1e-12, atol=1e-13)
+            dk_sum += dk_r
+            dv_sum += dv_r
+        np.testing.assert_allclose(dk_sum, dk[0, 0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dv_sum, dv[0, 0], rtol=1e-12, atol=1e-13)
 
 
 def test_row_block_does_not_change_results():
