@@ -14,7 +14,7 @@ Beside the headline number the line carries
   launch from rocprofv3 counters (profiles/traffic.json), or null when the
   kernel sources changed since the counters were taken;
 * ``cpu_baseline``: the fp64 oracle timed on this host on a bounded sample of
-  the same workload (the last 4096 query rows of one head).
+  the same workload (about 10 s of row blocks, see cpu_baseline).
 
 Other modes: ``--all`` prints a table over every workload (and the causal
 comparator of each packed one); ``--copy-calibration`` runs a plain
@@ -175,16 +175,19 @@ def run_workload(w, steps: int, warmup: int, seg_override="keep", causal=True, q
     return res
 
 
-CPU_SAMPLE_ROWS = 4096
+CPU_BLOCK_ROWS = 1024
+CPU_TARGET_SECONDS = 10.0
 
 
 def cpu_baseline(w, t_np, seg_np, causal=True):
     """The fp64 oracle on a bounded sample of the workload, on this host's cores.
 
-    Sample: the last CPU_SAMPLE_ROWS query rows of (batch 0, head 0), forward
-    (O, LSE) and backward (dQ of those rows and their dK, dV contributions),
-    each with the explicit mask over all N keys.  Credited flops are 14 * D
-    times the visible pairs of those rows."""
+    The sample is made of blocks of CPU_BLOCK_ROWS query rows, taken from the
+    end of (batch 0, head 0) backwards, then head 1, ..., until about
+    CPU_TARGET_SECONDS of oracle work: per block the forward (O, LSE of those
+    rows) and the backward (their dQ and their dK, dV contributions), each with
+    the explicit mask over all N keys.  Credited flops are 14 * D times the
+    visible pairs of the rows done."""
     import numpy as np
 
     from oracle import attention_backward_rows, attention_rows, visible_mask
@@ -193,21 +196,30 @@ def cpu_baseline(w, t_np, seg_np, causal=True):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
-    b, h = 0, 0
-    R = min(CPU_SAMPLE_ROWS, w.N)
-    rows = np.arange(w.N - R, w.N)
-    s = {n: a[b, h] for n, a in t_np.items()}
+    b = 0
     seg_row = None if seg_np is None else seg_np[b]
+    V, nrows, heads, el = 0, 0, set(), 0.0
     t0 = time.perf_counter()
-    o_r, lse_r = attention_rows(s["q"], s["k"], s["v"], rows, seg_row, w.scale, causal)
-    attention_backward_rows(s["q"], s["k"], s["v"], s["do"], o_r, lse_r, rows, seg_row, w.scale, causal)
-    el = time.perf_counter() - t0
-    V = int(visible_mask(rows, w.N, seg_row, causal).sum())
+    for h in range(w.H):
+        s = {n: a[b, h] for n, a in t_np.items()}
+        for hi in range(w.N, 0, -CPU_BLOCK_ROWS):
+            rows = np.arange(max(0, hi - CPU_BLOCK_ROWS), hi)
+            o_r, lse_r = attention_rows(s["q"], s["k"], s["v"], rows, seg_row, w.scale, causal)
+            attention_backward_rows(s["q"], s["k"], s["v"], s["do"], o_r, lse_r, rows, seg_row,
+                                    w.scale, causal)
+            V += int(visible_mask(rows, w.N, seg_row, causal).sum())
+            nrows += rows.size
+            heads.add(h)
+            el = time.perf_counter() - t0
+            if el >= CPU_TARGET_SECONDS:
+                break
+        if el >= CPU_TARGET_SECONDS:
+            break
     return {"value": round(14.0 * w.D * V / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"query rows [{w.N - R}, {w.N}) of (batch 0, head 0), N={w.N}, D={w.D}: fp64 "
-                      f"forward + backward with the explicit mask over all keys ({V} visible pairs, "
-                      f"{el:.1f} s); cores = BLAS threads",
+            "sample": f"{nrows} query rows of batch 0 over {len(heads)} head(s), last rows first, of "
+                      f"N={w.N}, D={w.D}: fp64 forward + backward with the explicit mask over all keys "
+                      f"({V} visible pairs, {el:.1f} s); cores = BLAS threads",
             "seconds": round(el, 2)}
 
 
