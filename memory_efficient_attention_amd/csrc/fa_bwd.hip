@@ -52,15 +52,17 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
-// One workgroup = 4 waves x 32 queries; walks the key tiles the query tile can
+// One workgroup = 8 waves x 32 queries; walks the key tiles the query tile can
 // see.  Per tile: S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T held in registers),
 // P^T and dS^T in registers, dQ^T += K^T dS^T with K^T through the transposing
 // LDS read of the K tile.
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
-  constexpr int NW = FWD_WAVES, NT = NW * 64, BM = FWD_BM, BN = KEY_TILE;
+  constexpr int NW = FWD_WAVES, BM = FWD_BM, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
-  constexpr int TILE = BN * D * (int)sizeof(T);
+  using L = Layout<T, D>;
+  using St = Stager<T, BN, D, NW>;
+  constexpr int TILE = L::bytes(BN);
   __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE + 2 * BN * 4];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
 
@@ -71,9 +73,9 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
   const int nqt = p.ntiles;
 
   const int total = p.B * p.H * nqt;
-  const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / nqt;
-  const int qt = nqt - 1 - (L - bh * nqt);
+  const int Lw = xcd_remap(blockIdx.x, total);
+  const int bh = Lw / nqt;
+  const int qt = nqt - 1 - (Lw - bh * nqt);
   const int b = bh / p.H;
   const size_t off = (size_t)bh * N * D;
   const T* gq = (const T*)p.q + off;
@@ -114,13 +116,18 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
   }
   const float c = p.c;
 
+  St st;
+  st.init(wave, lane);
+  const int rbase = L::row_base(lane);
+  const int cbase = L::col_base(lane);
+
   f32x16 dqacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
 
   auto stage = [&](int kt, int buf) {
-    stage_tile<T, BN, D, NT>(smem + buf * TILE, gk, kt * BN, N, wave, lane);
-    stage_tile<T, BN, D, NT>(smem + (2 + buf) * TILE, gv, kt * BN, N, wave, lane);
+    st.issue(smem + buf * TILE, gk, kt * BN, N, wave);
+    st.issue(smem + (2 + buf) * TILE, gv, kt * BN, N, wave);
     if (packed) stage_vec<BN>(smem + 4 * TILE + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
   };
 
@@ -157,8 +164,8 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        mma(sacc[kb], frag_row<T, D>(Ks, 32 * kb + col, 2 * ks + h), qf[ks]);
-        mma(dpacc[kb], frag_row<T, D>(Vs, 32 * kb + col, 2 * ks + h), dof[ks]);
+        mma(sacc[kb], frag_row<T, D>(Ks, rbase, 32 * kb, ks), qf[ks]);
+        mma(dpacc[kb], frag_row<T, D>(Vs, rbase, 32 * kb, ks), dof[ks]);
       }
     }
 
@@ -194,23 +201,25 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
-          mma(dqacc[db], frag_col<T, D>(Ks, 32 * kb + 16 * kc, 32 * db, lane), dsf[kb][kc]);
+          mma(dqacc[db], frag_col<T, D>(Ks, cbase, 32 * kb + 16 * kc, 32 * db), dsf[kb][kc]);
   }
 
   if (qi < N) store_rows<T, D>((T*)p.dq + off, qi, dqacc, p.scale, lane);
 }
 
 // ---------------------------------------------------------------- dK / dV
-// One workgroup = 4 waves x 32 keys; walks the query tiles that can see the
+// One workgroup = 8 waves x 32 keys; walks the query tiles that can see the
 // key tile.  Per tile: S = Q K^T and dP = dO V^T (K^T, V^T held in registers;
 // the accumulator columns are keys, rows queries), P and dS in registers,
 // dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T through the transposing
 // LDS read.
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p) {
-  constexpr int NW = DKV_WAVES, NT = NW * 64, BNK = DKV_BN, BMQ = QRY_TILE;
+  constexpr int NW = DKV_WAVES, BNK = DKV_BN, BMQ = QRY_TILE;
   constexpr int KS = D / 16, DB = D / 32, QB = BMQ / 32;
-  constexpr int TILE = BMQ * D * (int)sizeof(T);
+  using L = Layout<T, D>;
+  using St = Stager<T, BMQ, D, NW>;
+  constexpr int TILE = L::bytes(BMQ);
   constexpr int VEC = BMQ * 4;
   __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE + 6 * VEC];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
@@ -223,9 +232,9 @@ __global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p)
   const int nkt = p.ntiles;
 
   const int total = p.B * p.H * nkt;
-  const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / nkt;
-  const int kt = L - bh * nkt;       // causal: key tile 0 sees the most queries
+  const int Lw = xcd_remap(blockIdx.x, total);
+  const int bh = Lw / nkt;
+  const int kt = Lw - bh * nkt;       // causal: key tile 0 sees the most queries
   const int b = bh / p.H;
   const size_t off = (size_t)bh * N * D;
   const T* gq = (const T*)p.q + off;
@@ -267,6 +276,11 @@ __global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p)
   }
   const float c = p.c;
 
+  St st;
+  st.init(wave, lane);
+  const int rbase = L::row_base(lane);
+  const int cbase = L::col_base(lane);
+
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -276,8 +290,8 @@ __global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p)
 
   auto stage = [&](int qt, int buf) {
     const int r0 = qt * BMQ;
-    stage_tile<T, BMQ, D, NT>(smem + buf * TILE, gq, r0, N, wave, lane);
-    stage_tile<T, BMQ, D, NT>(smem + (2 + buf) * TILE, gdo, r0, N, wave, lane);
+    st.issue(smem + buf * TILE, gq, r0, N, wave);
+    st.issue(smem + (2 + buf) * TILE, gdo, r0, N, wave);
     stage_vec<BMQ>(smem + 4 * TILE + buf * VEC, glse2, r0, N, wave, 0, lane);
     stage_vec<BMQ>(smem + 4 * TILE + (2 + buf) * VEC, gdelta, r0, N, wave, 1 % NW, lane);
     if (packed) stage_vec<BMQ>(smem + 4 * TILE + (4 + buf) * VEC, seg, r0, N, wave, 2 % NW, lane);
@@ -318,8 +332,8 @@ __global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p)
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        mma(sacc[qb], frag_row<T, D>(Qs, 32 * qb + col, 2 * ks + h), kf[ks]);
-        mma(dpacc[qb], frag_row<T, D>(dOs, 32 * qb + col, 2 * ks + h), vf[ks]);
+        mma(sacc[qb], frag_row<T, D>(Qs, rbase, 32 * qb, ks), kf[ks]);
+        mma(dpacc[qb], frag_row<T, D>(dOs, rbase, 32 * qb, ks), vf[ks]);
       }
     }
 
@@ -361,8 +375,8 @@ __global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p)
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          mma(dvacc[db], frag_col<T, D>(dOs, 32 * qb + 16 * kc, 32 * db, lane), pf[qb][kc]);
-          mma(dkacc[db], frag_col<T, D>(Qs, 32 * qb + 16 * kc, 32 * db, lane), dsf[qb][kc]);
+          mma(dvacc[db], frag_col<T, D>(dOs, cbase, 32 * qb + 16 * kc, 32 * db), pf[qb][kc]);
+          mma(dkacc[db], frag_col<T, D>(Qs, cbase, 32 * qb + 16 * kc, 32 * db), dsf[qb][kc]);
         }
   }
 

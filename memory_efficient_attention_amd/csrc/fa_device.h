@@ -69,53 +69,82 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32); }
 
 // ---------------------------------------------------------------- LDS tiles
-// A tile holds ROWS rows of D elements, row-major, rows packed back to back
-// (row stride D * sizeof(T) bytes).  For bf16 the 16-byte chunks of a row
-// are permuted by an XOR with swz(row) so that both read patterns used here
-// hit 64 distinct banks: 16 lanes reading one chunk column of 16 consecutive
-// rows (frag_row), and 32 lanes reading 4 rows x 4 chunks (frag_col).
+// A tile holds ROWS rows of D elements.  For bf16, rows sit in groups of 4:
+// inside a group consecutive rows are S1 = row + 64 bytes apart, groups are
+// S4 = 4 * S1 + 16 bytes apart.  With 64 four-byte banks this makes both read
+// patterns used here conflict-free: 16 lanes reading the same 16-byte column
+// chunk of 16 consecutive rows (frag_row: the 16 row starts fall on distinct
+// 4-bank groups), and 32 lanes reading 4 consecutive rows x 64 bytes
+// (frag_col: the 4 row starts are 16 banks apart).  Every fragment address is
+// then a per-lane base plus a compile-time offset.  fp32 tiles (small shapes
+// only) are packed without padding.
 template <typename T, int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (sizeof(T) != 2) {
-    return 0;
-  } else if constexpr (D == 128) {
-    return ((row & 3) << 2) | ((row >> 2) & 3);
-  } else {
-    static_assert(D == 64, "head_dim");
-    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  }
-}
-
-template <typename T, int D>
-__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return (uint32_t)(row * D * (int)sizeof(T) + ((chunk ^ swz<T, D>(row)) << 4));
-}
-
-// Issue direct global->LDS loads of rows [row0, row0 + ROWS) of a (N, D)
-// matrix into a tile.  Rows >= N read row N - 1 (finite data the masks
-// discard).  Each wave instruction fills 64 consecutive 16-byte LDS chunks;
-// the swizzle is applied by choosing which global chunk each lane fetches.
-template <typename T, int ROWS, int D, int NT>
-__device__ __forceinline__ void stage_tile(FA_LDS char* tile, const T* g, int row0, int N,
-                                           int wave, int lane) {
-  constexpr int CPR = D * (int)sizeof(T) / 16;
-  constexpr int CHUNKS = ROWS * CPR;
-  static_assert(CHUNKS % 64 == 0, "tile must be a whole number of wave loads");
-  constexpr int WAVES = NT / 64;
-#pragma unroll
-  for (int base = 0; base < CHUNKS; base += NT) {
-    const int wbase = base + wave * 64;
-    if (CHUNKS % NT == 0 || wbase < CHUNKS) {
-      const int P = wbase + lane;
-      const int r = P / CPR;
-      const int c = (P % CPR) ^ swz<T, D>(r);
-      const int gr = min(row0 + r, N - 1);
-      const char* src = (const char*)(g + (size_t)gr * D) + (c << 4);
-      __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)(tile + wbase * 16), 16, 0, 0);
+struct Layout {
+  static constexpr int ROW = D * (int)sizeof(T);
+  static constexpr int S1 = sizeof(T) == 2 ? ROW + 64 : ROW;
+  static constexpr int S4 = sizeof(T) == 2 ? 4 * S1 + 16 : 4 * ROW;
+  static constexpr int bytes(int rows) { return (rows / 4) * S4; }
+  // byte offset of a row; linear in (row / 4, row % 4), so off(a + b) =
+  // off(a) + off(b) whenever a is a multiple of 4
+  __device__ static constexpr int off(int row) { return (row >> 2) * S4 + (row & 3) * S1; }
+  // frag_row lane base: row lane % 32, 8-element chunk parity lane / 32
+  __device__ static int row_base(int lane) { return off(lane & 31) + (lane >> 5) * 8 * (int)sizeof(T); }
+  // frag_col lane base (see frag_col)
+  __device__ static int col_base(int lane) {
+    const int h = lane >> 5;
+    if constexpr (sizeof(T) == 2) {
+      const int g = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
+      return h * S4 + r * S1 + (16 * (g & 1) + 4 * c) * 2;
+    } else {
+      return h * S4 + (lane & 31) * 4;
     }
   }
-  (void)WAVES;
-}
+};
+
+// Direct global->LDS staging of ROWS rows of a (N, D) matrix into a tile.
+// Each wave instruction fills 64 consecutive 16-byte LDS chunks; the lanes
+// whose chunk is padding stay idle.  init() precomputes, per lane and per
+// instruction, the source byte offset relative to the tile's first row.
+// Rows >= N read row N - 1 (finite data that the masks discard).
+template <typename T, int ROWS, int D, int NW>
+struct Stager {
+  using L = Layout<T, D>;
+  static constexpr int CS1 = L::S1 / 16, CS4 = L::S4 / 16, CROW = L::ROW / 16;
+  static constexpr int NCH = (ROWS / 4) * CS4;
+  static constexpr int NINST = (NCH + 63) / 64;
+  static constexpr int PER = (NINST + NW - 1) / NW;
+  static constexpr int ROW_SHIFT = __builtin_ctz(L::ROW);
+  static_assert((L::ROW & (L::ROW - 1)) == 0, "row bytes must be a power of two");
+  int src[PER];
+
+  __device__ void init(int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int P = (k * NW + wave) * 64 + lane;
+      const int g = P / CS4, w = P % CS4, b = w / CS1, c = w % CS1;
+      src[k] = (P < NCH && b < 4 && c < CROW) ? ((4 * g + b) * L::ROW + c * 16) : -1;
+    }
+  }
+
+  __device__ void issue(FA_LDS char* tile, const T* g, int row0, int N, int wave) const {
+    const char* gb = (const char*)g;
+    const bool whole = row0 + ROWS <= N;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int inst = k * NW + wave;
+      if (inst < NINST && src[k] >= 0) {
+        const char* ptr;
+        if (whole) {
+          ptr = gb + (size_t)row0 * L::ROW + src[k];
+        } else {
+          const int r = min(row0 + (src[k] >> ROW_SHIFT), N - 1);
+          ptr = gb + (size_t)r * L::ROW + (src[k] & (L::ROW - 1));
+        }
+        __builtin_amdgcn_global_load_lds(ptr, (FA_LDS void*)(tile + inst * 1024), 16, 0, 0);
+      }
+    }
+  }
+};
 
 // Direct global->LDS load of ROWS consecutive 4-byte values (row0 + i, i <
 // ROWS, clamped to N - 1) by wave `wave_id` of the workgroup.
@@ -135,15 +164,18 @@ __device__ __forceinline__ void stage_vec(FA_LDS char* dst, const void* g, int r
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// 8 consecutive elements of `row` starting at column 8 * c8 (A/B fragment
-// along D).
+// A/B fragment along D: 8 consecutive elements of tile row rb + lane % 32 at
+// column 8 * (2 * ks + lane / 32); rb is a multiple of 4, `base` =
+// Layout::row_base(lane).
 template <typename T, int D>
-__device__ __forceinline__ frag_t<T> frag_row(const FA_LDS char* tile, int row, int c8) {
+__device__ __forceinline__ frag_t<T> frag_row(const FA_LDS char* tile, int base, int rb, int ks) {
+  using L = Layout<T, D>;
+  const FA_LDS char* p = tile + base + L::off(rb) + ks * 16 * (int)sizeof(T);
   if constexpr (sizeof(T) == 2) {
-    return *(const FA_LDS bf16x8*)(tile + tile_off<T, D>(row, c8));
+    return *(const FA_LDS bf16x8*)p;
   } else {
-    const FA_LDS f32x4* p = (const FA_LDS f32x4*)(tile + tile_off<T, D>(row, 2 * c8));
-    f32x4 a = p[0], b = p[1];
+    const FA_LDS f32x4* q = (const FA_LDS f32x4*)p;
+    f32x4 a = q[0], b = q[1];
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   }
 }
@@ -152,7 +184,8 @@ __device__ __forceinline__ frag_t<T> frag_row(const FA_LDS char* tile, int row, 
 //   tile[kbase + 4h + s][col0 + l%32]      for s = 0..3, then
 //   tile[kbase + 8 + 4h + s][col0 + l%32]  for s = 0..3,
 // i.e. the A operand whose k-slots match acc_frag(acc, kc) of a product whose
-// accumulator rows are tile rows kbase .. kbase + 15.
+// accumulator rows are tile rows kbase .. kbase + 15 (kbase a multiple of 16;
+// `base` = Layout::col_base(lane)).
 //
 // bf16 uses ds_read_b64_tr_b16: within each 16-lane group, lane i receives
 // element i%4 of the 8 bytes fetched by lanes 4r + i/4 (r = 0..3).  So lane
@@ -160,26 +193,19 @@ __device__ __forceinline__ frag_t<T> frag_row(const FA_LDS char* tile, int row, 
 // col0 + 16(g%2) + 4c .. +3, and lane 16g + i ends up with column
 // col0 + 16(g%2) + i of rows kbase + 4h + 0..3.
 template <typename T, int D>
-__device__ __forceinline__ frag_t<T> frag_col(const FA_LDS char* tile, int kbase, int col0, int lane) {
-  const int h = lane >> 5;
+__device__ __forceinline__ frag_t<T> frag_col(const FA_LDS char* tile, int base, int kbase, int col0) {
+  using L = Layout<T, D>;
+  const FA_LDS char* p = tile + base + L::off(kbase) + col0 * (int)sizeof(T);
   if constexpr (sizeof(T) == 2) {
-    const int g = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
-    const int e = col0 + 16 * (g & 1) + 4 * c;
-    const int row1 = kbase + 4 * h + r, row2 = row1 + 8;
-    const uint32_t off1 = tile_off<T, D>(row1, e >> 3) + ((e & 4) << 1);
-    const uint32_t off2 = tile_off<T, D>(row2, e >> 3) + ((e & 4) << 1);
-    s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(tile + off1));
-    s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(tile + off2));
+    s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)p);
+    s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(p + 2 * L::S4));
     bf16x4 xb = __builtin_bit_cast(bf16x4, x), yb = __builtin_bit_cast(bf16x4, y);
     return bf16x8{xb[0], xb[1], xb[2], xb[3], yb[0], yb[1], yb[2], yb[3]};
   } else {
-    const int col = col0 + (lane & 31);
     f32x8 out;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int row = kbase + (s < 4 ? 4 * h + s : 8 + 4 * h + (s - 4));
-      out[s] = *(const FA_LDS float*)(tile + row * D * 4 + col * 4);
-    }
+    for (int s = 0; s < 8; ++s)
+      out[s] = *(const FA_LDS float*)(p + (s >= 4 ? 2 * L::S4 : 0) + (s & 3) * L::S1);
     return out;
   }
 }

@@ -6,15 +6,17 @@
 // packed rows, block-diagonal by segment id (same README, "Sequence packing";
 // changelog "Added": the PACKED forward variant).
 //
-// One workgroup = 4 waves = 128 queries of one (batch, head).  Each wave owns
+// One workgroup = 8 waves = 256 queries of one (batch, head).  Each wave owns
 // 32 queries and computes S^T = K Q^T for a 64-key tile (two 32x32 MFMA
 // tiles), so the softmax statistics of a query live in one lane pair (l,
 // l+32).  Q^T stays in registers for the whole key walk; K and V tiles are
 // double-buffered in LDS with direct global->LDS loads.  O^T += V^T P^T takes
-// P^T straight from the accumulator and V^T from the row-major V tile through
-// the transposing LDS read.  Causal / packed structure is used at wave
+// P^T straight from the accumulator and V^T from the V tile through the
+// transposing LDS read.  Causal / packed structure is used at wave
 // granularity: key tiles no query of a wave can see are skipped, tiles every
-// query sees fully skip the per-element mask.
+// query sees fully skip the per-element mask.  The running reference max
+// moves only when a row's max grows by more than 2^RESCALE_LOG2, so the O
+// rescale is a rare, wave-uniform branch.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -22,9 +24,11 @@ namespace fa {
 
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) {
-  constexpr int NW = FWD_WAVES, NT = NW * 64, BM = FWD_BM, BN = KEY_TILE;
+  constexpr int NW = FWD_WAVES, BM = FWD_BM, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
-  constexpr int TILE = BN * D * (int)sizeof(T);
+  using L = Layout<T, D>;
+  using St = Stager<T, BN, D, NW>;
+  constexpr int TILE = L::bytes(BN);
   __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE + 2 * BN * 4];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
 
@@ -34,9 +38,9 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
   const int N = p.N;
 
   const int total = p.B * p.H * p.nqt;
-  const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / p.nqt;
-  const int qt = p.nqt - 1 - (L - bh * p.nqt);   // longest query tiles first
+  const int Lw = xcd_remap(blockIdx.x, total);
+  const int bh = Lw / p.nqt;
+  const int qt = p.nqt - 1 - (Lw - bh * p.nqt);   // longest query tiles first
   const int b = bh / p.H;
   const size_t off = (size_t)bh * N * D;
   const T* gq = (const T*)p.q + off;
@@ -70,15 +74,21 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
     segq_last = seg[qlast];
   }
 
+  St st;
+  st.init(wave, lane);
+  const int rbase = L::row_base(lane);
+  const int cbase = L::col_base(lane);
+
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY, lsum = 0.f;
+  float msc = -INFINITY;   // reference max of the row, times c (log2 units)
+  float lsum = 0.f;        // this lane's half of the row sum, relative to msc
   const float c = p.c;
 
   auto stage = [&](int kt, int buf) {
-    stage_tile<T, BN, D, NT>(smem + buf * TILE, gk, kt * BN, N, wave, lane);
-    stage_tile<T, BN, D, NT>(smem + (2 + buf) * TILE, gv, kt * BN, N, wave, lane);
+    st.issue(smem + buf * TILE, gk, kt * BN, N, wave);
+    st.issue(smem + (2 + buf) * TILE, gv, kt * BN, N, wave);
     if (packed) stage_vec<BN>(smem + 4 * TILE + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
   };
 
@@ -114,9 +124,7 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        mma(sacc[kb], frag_row<T, D>(Ks, 32 * kb + col, 2 * ks + h), qf[ks]);
-      }
+      for (int kb = 0; kb < KB; ++kb) mma(sacc[kb], frag_row<T, D>(Ks, rbase, 32 * kb, ks), qf[ks]);
     }
 
     if (!full) {
@@ -136,32 +144,36 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
       }
     }
 
-    // Online softmax (base 2).  Both lanes of a pair hold the same query and
-    // share its running max; the running sum stays split until the end.
+    // Online softmax in base 2 with a lazily moved reference max.  Both lanes
+    // of a pair hold the same query and take the same decisions.
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
     tmax = fmaxf(tmax, other_half(tmax));
-    const float mnew = fmaxf(m, tmax);
-    const float msc = (mnew == -INFINITY) ? 0.f : mnew * c;
-    const float alpha = exp2_fast(m * c - msc);
-    m = mnew;
-    float ps = 0.f;
+    const float tsc = tmax * c;
+    const bool grow = tsc > msc + RESCALE_LOG2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      // alpha is 1 for rows that keep their reference (also when it is still
+      // -inf: no visible key yet), and 0 for a row's first visible tile.
+      const float alpha = grow ? exp2_fast(msc - tsc) : 1.f;
+      msc = grow ? tsc : msc;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float mref = (msc == -INFINITY) ? 0.f : msc;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2_fast(fmaf(sacc[kb][r], c, -msc));
+        const float e = exp2_fast(fmaf(sacc[kb][r], c, -mref));
         sacc[kb][r] = e;
-        ps += e;
+        lsum += e;
       }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
 
     // O^T += V^T P^T.
     frag_t<T> pf[KB][2];
@@ -176,13 +188,13 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
-          mma(oacc[db], frag_col<T, D>(Vs, 32 * kb + 16 * kc, 32 * db, lane), pf[kb][kc]);
+          mma(oacc[db], frag_col<T, D>(Vs, cbase, 32 * kb + 16 * kc, 32 * db), pf[kb][kc]);
   }
 
   const float lt = lsum + other_half(lsum);
   if (qi < N) {
     store_rows<T, D>((T*)p.o + off, qi, oacc, 1.f / lt, lane);
-    if (h == 0) p.lse[(size_t)bh * N + qi] = (m * c + log2_fast(lt)) * kLn2;
+    if (h == 0) p.lse[(size_t)bh * N + qi] = (msc + log2_fast(lt)) * kLn2;
   }
 }
 

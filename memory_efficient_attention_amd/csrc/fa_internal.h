@@ -10,12 +10,17 @@ namespace fa {
 // Tile sizes.  Forward and dQ: one workgroup owns FWD_WAVES * 32 queries and
 // walks key tiles of KEY_TILE keys.  dK/dV: one workgroup owns DKV_WAVES * 32
 // keys and walks query tiles of QRY_TILE queries.
-constexpr int FWD_WAVES = 4;
+constexpr int FWD_WAVES = 8;
 constexpr int FWD_BM = FWD_WAVES * 32;
 constexpr int KEY_TILE = 64;
 constexpr int DKV_WAVES = 4;
 constexpr int DKV_BN = DKV_WAVES * 32;
 constexpr int QRY_TILE = 32;
+
+// Online-softmax reference max: moved only when a row's max exceeds it by
+// more than this many powers of two, so the O accumulator is rescaled rarely;
+// unnormalised probabilities stay below 2^RESCALE_LOG2.
+constexpr float RESCALE_LOG2 = 8.f;
 
 struct FwdParams {
   const void* q;
