@@ -48,24 +48,30 @@ def _run(cmd: list[str], verbose: bool) -> None:
         print(out)
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every HIP source for gfx950 and link libfa.so; returns its path."""
+def build(verbose: bool = False, jobs: int | None = None, out: str | None = None,
+          defines: tuple[str, ...] = (), build_dir: str | None = None) -> str:
+    """Compile every HIP source for gfx950 and link libfa.so; returns its path.
+
+    ``out``/``defines``/``build_dir`` build a tuning variant elsewhere (e.g.
+    defines=("FA_QRY_TILE=64",)); the default builds the package library."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    bdir = build_dir or BUILD_DIR
+    lib_path = out or LIB_PATH
+    os.makedirs(bdir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

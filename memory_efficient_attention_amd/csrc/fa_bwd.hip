@@ -322,21 +322,48 @@ __global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p)
     }
     if (skip) continue;
 
+    // Visibility bits of this lane's 16 accumulator elements per query block
+    // (bit 4j + i: query 32qb + 8j + 4h + i of the tile, key kj).  Computed
+    // before the products so that the tile's MFMA / VALU work below is one
+    // branch-free region the scheduler can interleave.
+    uint32_t vis[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) vis[qb] = 0xFFFFu;
+    if (!full) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qr = 32 * qb + 8 * j + 4 * h;
+          const i32x4 sq = packed ? *(const FA_LDS i32x4*)(sqs + qr) : i32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int q = q0 + qr + i;
+            const bool v = q < N && kj < N && (!CAUSAL || kj <= q) && (!packed || sq[i] == segk);
+            bits |= (v ? 1u : 0u) << (4 * j + i);
+          }
+        }
+        vis[qb] = bits;
+      }
+    }
+
+    // S = Q K^T and dP = dO V^T, block by block.
     f32x16 sacc[QB], dpacc[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       sacc[qb] = f32x16{};
       dpacc[qb] = f32x16{};
-    }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+      for (int ks = 0; ks < KS; ++ks) {
         mma(sacc[qb], frag_row<T, D>(Qs, rbase, 32 * qb, ks), kf[ks]);
         mma(dpacc[qb], frag_row<T, D>(dOs, rbase, 32 * qb, ks), vf[ks]);
       }
     }
 
+    // Per block: P = exp2(S c - lse2), dS = P (dP - D_i); then dV^T += dO^T P
+    // and dK^T += Q^T dS.  Block qb's VALU work can run under block qb+1's
+    // MFMAs.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -344,40 +371,28 @@ __global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p)
         const int qr = 32 * qb + 8 * j + 4 * h;
         const f32x4 l2 = *(const FA_LDS f32x4*)(l2s + qr);
         const f32x4 dl = *(const FA_LDS f32x4*)(dls + qr);
-        i32x4 sq = (packed && !full) ? *(const FA_LDS i32x4*)(sqs + qr) : i32x4{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float s = sacc[qb][4 * j + i];
-          if (!full) {
-            const int q = q0 + qr + i;
-            const bool vis = q < N && kj < N && (!CAUSAL || kj <= q) && (!packed || sq[i] == segk);
-            if (!vis) s = -INFINITY;
-          }
-          const float pv = exp2_fast(fmaf(s, c, -l2[i]));
+          const float sv = ((vis[qb] >> (4 * j + i)) & 1u) ? sacc[qb][4 * j + i] : -INFINITY;
+          const float pv = exp2_fast(fmaf(sv, c, -l2[i]));
           sacc[qb][4 * j + i] = pv;
           dpacc[qb][4 * j + i] = pv * (dpacc[qb][4 * j + i] - dl[i]);
         }
       }
-    }
-
-    frag_t<T> pf[QB][2], dsf[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+      frag_t<T> pf[2], dsf[2];
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        pf[qb][kc] = acc_frag<T>(sacc[qb], kc);
-        dsf[qb][kc] = acc_frag<T>(dpacc[qb], kc);
+        pf[kc] = acc_frag<T>(sacc[qb], kc);
+        dsf[kc] = acc_frag<T>(dpacc[qb], kc);
       }
-    }
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          mma(dvacc[db], frag_col<T, D>(dOs, cbase, 32 * qb + 16 * kc, 32 * db), pf[qb][kc]);
-          mma(dkacc[db], frag_col<T, D>(Qs, cbase, 32 * qb + 16 * kc, 32 * db), dsf[qb][kc]);
+          mma(dvacc[db], frag_col<T, D>(dOs, cbase, 32 * qb + 16 * kc, 32 * db), pf[kc]);
+          mma(dkacc[db], frag_col<T, D>(Qs, cbase, 32 * qb + 16 * kc, 32 * db), dsf[kc]);
         }
+    }
   }
 
   if (kj < N) {

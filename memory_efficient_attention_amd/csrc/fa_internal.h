@@ -10,12 +10,25 @@ namespace fa {
 // Tile sizes.  Forward and dQ: one workgroup owns FWD_WAVES * 32 queries and
 // walks key tiles of KEY_TILE keys.  dK/dV: one workgroup owns DKV_WAVES * 32
 // keys and walks query tiles of QRY_TILE queries.
-constexpr int FWD_WAVES = 8;
+// (Each can be overridden at build time with -DFA_<NAME>=value for tuning.)
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 8
+#endif
+#ifndef FA_KEY_TILE
+#define FA_KEY_TILE 64
+#endif
+#ifndef FA_DKV_WAVES
+#define FA_DKV_WAVES 8
+#endif
+#ifndef FA_QRY_TILE
+#define FA_QRY_TILE 32
+#endif
+constexpr int FWD_WAVES = FA_FWD_WAVES;
 constexpr int FWD_BM = FWD_WAVES * 32;
-constexpr int KEY_TILE = 64;
-constexpr int DKV_WAVES = 4;
+constexpr int KEY_TILE = FA_KEY_TILE;
+constexpr int DKV_WAVES = FA_DKV_WAVES;
 constexpr int DKV_BN = DKV_WAVES * 32;
-constexpr int QRY_TILE = 32;
+constexpr int QRY_TILE = FA_QRY_TILE;
 
 // Online-softmax reference max: moved only when a row's max exceeds it by
 // more than this many powers of two, so the O accumulator is rescaled rarely;
