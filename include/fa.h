@@ -69,8 +69,10 @@ typedef enum fa_dtype {
     FA_FP32 = 1
 } fa_dtype;
 
-/* Largest supported sequence length (rows per head). */
-#define FA_MAX_N (1 << 24)
+/* Largest supported sequence length (rows per head).  In addition one head's
+ * (N, D) matrix must stay below 2^31 bytes (N * D * element size), else
+ * FA_ERR_SHAPE. */
+#define FA_MAX_N (1 << 22)
 
 /*
  * Bytes of workspace fa_fwd (for_bwd = 0) or fa_bwd (for_bwd = 1) needs for

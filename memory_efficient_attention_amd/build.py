@@ -49,7 +49,8 @@ def _run(cmd: list[str], verbose: bool) -> None:
 
 
 def build(verbose: bool = False, jobs: int | None = None, out: str | None = None,
-          defines: tuple[str, ...] = (), build_dir: str | None = None) -> str:
+          defines: tuple[str, ...] = (), build_dir: str | None = None,
+          extra_flags: tuple[str, ...] = ()) -> str:
     """Compile every HIP source for gfx950 and link libfa.so; returns its path.
 
     ``out``/``defines``/``build_dir`` build a tuning variant elsewhere (e.g.
@@ -63,7 +64,8 @@ def build(verbose: bool = False, jobs: int | None = None, out: str | None = None
     for src in SOURCES:
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *FLAGS, *extra_flags, *[f"-D{d}" for d in defines], "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:

@@ -89,6 +89,8 @@ fa_status common_checks(int B, int H, int N, int D, fa_dtype dtype, float scale)
   if (!shape_ok(B, H, N)) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_DTYPE;
+  // one head's (N, D) matrix is addressed with 32-bit byte offsets
+  if ((long long)N * D * (dtype == FA_FP32 ? 4 : 2) >= (1LL << 31)) return FA_ERR_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   return FA_OK;
 }
@@ -175,7 +177,7 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
 
   if (seg) {
     if (fa::launch_seg_check(seg, B, N, (int32_t*)(w + L.flag), s) != hipSuccess) return FA_ERR_HIP;
-    if (fa::launch_qtile_table(seg, B, N, fa::FWD_BM, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
+    if (fa::launch_qtile_table(seg, B, N, fa::DQ_BM, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
         hipSuccess)
       return FA_ERR_HIP;
     if (fa::launch_ktile_table(seg, B, N, fa::DKV_BN, fa::QRY_TILE, causal != 0, (int2*)(w + L.ktab), s) !=
@@ -217,7 +219,7 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
 
   if (!record(events, 2, s)) return FA_ERR_HIP;
   p.tab = seg ? (const int2*)(w + L.qtab) : nullptr;
-  p.ntiles = (N + fa::FWD_BM - 1) / fa::FWD_BM;
+  p.ntiles = (N + fa::DQ_BM - 1) / fa::DQ_BM;
   if (fa::launch_bwd_dq(p, dt, D, causal != 0, s) != hipSuccess) return FA_ERR_HIP;
   if (!record(events, 3, s)) return FA_ERR_HIP;
   return FA_OK;

@@ -52,18 +52,22 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
-// One workgroup = 8 waves x 32 queries; walks the key tiles the query tile can
+// One workgroup = 4 waves x 32 queries; walks the key tiles the query tile can
 // see.  Per tile: S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T held in registers),
 // P^T and dS^T in registers, dQ^T += K^T dS^T with K^T through the transposing
 // LDS read of the K tile.
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
-  constexpr int NW = FWD_WAVES, BM = FWD_BM, BN = KEY_TILE;
+__global__ void __launch_bounds__(DQ_WAVES * 64, FA_WAVES_PER_EU) dq_kernel(const BwdParams p) {
+  constexpr int NW = DQ_WAVES, BM = DQ_BM, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
-  using L = Layout<T, D>;
-  using St = Stager<T, BN, D, NW>;
-  constexpr int TILE = L::bytes(BN);
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE + 2 * BN * 4];
+  // K is read along rows and transposed (DUAL), V only along rows.
+  using LK = Layout<T, D, true>;
+  using LV = Layout<T, D, false>;
+  using StK = Stager<T, BN, D, NW, true>;
+  using StV = Stager<T, BN, D, NW, false>;
+  constexpr int TK = LK::bytes(BN), TV = LV::bytes(BN);
+  // layout: K[2] | V[2] | seg[2]
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * TK + 2 * TV + 2 * BN * 4];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -116,19 +120,22 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
   }
   const float c = p.c;
 
-  St st;
-  st.init(wave, lane);
-  const int rbase = L::row_base(lane);
-  const int cbase = L::col_base(lane);
+  StK stk;
+  StV stv;
+  stk.init(wave, lane);
+  stv.init(wave, lane);
+  const int kbase_r = LK::row_base(lane);
+  const int vbase_r = LV::row_base(lane);
+  const int cbase = LK::col_base(lane);
 
   f32x16 dqacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
 
   auto stage = [&](int kt, int buf) {
-    st.issue(smem + buf * TILE, gk, kt * BN, N, wave);
-    st.issue(smem + (2 + buf) * TILE, gv, kt * BN, N, wave);
-    if (packed) stage_vec<BN>(smem + 4 * TILE + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
+    stk.issue(smem + buf * TK, gk, kt * BN, N, wave);
+    stv.issue(smem + 2 * TK + buf * TV, gv, kt * BN, N, wave);
+    if (packed) stage_vec<BN>(smem + 2 * TK + 2 * TV + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
   };
 
   if (kt_lo <= kt_hi) stage(kt_lo, 0);
@@ -138,9 +145,9 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
     __syncthreads();
     if (kt < kt_hi) stage(kt + 1, buf ^ 1);
 
-    const FA_LDS char* Ks = smem + buf * TILE;
-    const FA_LDS char* Vs = smem + (2 + buf) * TILE;
-    const FA_LDS int* segk = (const FA_LDS int*)(smem + 4 * TILE + buf * BN * 4);
+    const FA_LDS char* Ks = smem + buf * TK;
+    const FA_LDS char* Vs = smem + 2 * TK + buf * TV;
+    const FA_LDS int* segk = (const FA_LDS int*)(smem + 2 * TK + 2 * TV + buf * BN * 4);
     const int k0 = kt * BN;
     const int klast = min(k0 + BN, N) - 1;
 
@@ -164,8 +171,8 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        mma(sacc[kb], frag_row<T, D>(Ks, rbase, 32 * kb, ks), qf[ks]);
-        mma(dpacc[kb], frag_row<T, D>(Vs, rbase, 32 * kb, ks), dof[ks]);
+        mma(sacc[kb], frag_row<T, D, true>(Ks, kbase_r, 32 * kb, ks), qf[ks]);
+        mma(dpacc[kb], frag_row<T, D, false>(Vs, vbase_r, 32 * kb, ks), dof[ks]);
       }
     }
 
@@ -208,13 +215,13 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK / dV
-// One workgroup = 8 waves x 32 keys; walks the query tiles that can see the
+// One workgroup = 4 waves x 32 keys; walks the query tiles that can see the
 // key tile.  Per tile: S = Q K^T and dP = dO V^T (K^T, V^T held in registers;
 // the accumulator columns are keys, rows queries), P and dS in registers,
 // dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T through the transposing
 // LDS read.
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(DKV_WAVES * 64) dkdv_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(DKV_WAVES * 64, FA_WAVES_PER_EU) dkdv_kernel(const BwdParams p) {
   constexpr int NW = DKV_WAVES, BNK = DKV_BN, BMQ = QRY_TILE;
   constexpr int KS = D / 16, DB = D / 32, QB = BMQ / 32;
   using L = Layout<T, D>;
@@ -419,7 +426,7 @@ hipError_t launch_bwd_pre(const PreParams& p, int dtype, int D, hipStream_t s) {
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
   const long long total = (long long)p.B * p.H * p.ntiles;
-  hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL>), dim3((unsigned)total), dim3(FWD_WAVES * 64), 0, s, p);
+  hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL>), dim3((unsigned)total), dim3(DQ_WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
 

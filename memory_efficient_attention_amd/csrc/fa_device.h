@@ -69,28 +69,32 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32); }
 
 // ---------------------------------------------------------------- LDS tiles
-// A tile holds ROWS rows of D elements.  For bf16, rows sit in groups of 4:
-// inside a group consecutive rows are S1 = row + 64 bytes apart, groups are
-// S4 = 4 * S1 + 16 bytes apart.  With 64 four-byte banks this makes both read
-// patterns used here conflict-free: 16 lanes reading the same 16-byte column
-// chunk of 16 consecutive rows (frag_row: the 16 row starts fall on distinct
-// 4-bank groups), and 32 lanes reading 4 consecutive rows x 64 bytes
-// (frag_col: the 4 row starts are 16 banks apart).  Every fragment address is
-// then a per-lane base plus a compile-time offset.  fp32 tiles (small shapes
-// only) are packed without padding.
-template <typename T, int D>
+// A tile holds ROWS rows of D elements; rows sit in groups of 4, consecutive
+// rows of a group S1 bytes apart, groups S4 bytes apart.  Two bf16 layouts,
+// both free of bank conflicts with 64 four-byte banks:
+//  * DUAL (tiles read both along rows and transposed): S1 = row + 64 bytes,
+//    S4 = 4 * S1 + 16.  16 lanes reading the same 16-byte chunk of 16
+//    consecutive rows (frag_row) start on 16 distinct 4-bank groups, and 32
+//    lanes reading 4 consecutive rows x 64 bytes (frag_col) start 16 banks
+//    apart.
+//  * row-only (frag_row only): S1 = row + 16 bytes, S4 = 4 * S1, i.e. a plain
+//    padded stride; 26 % smaller than DUAL at D = 128.
+// Every fragment address is a per-lane base plus a compile-time offset.  fp32
+// tiles (small shapes only) are packed without padding.
+template <typename T, int D, bool DUAL = true>
 struct Layout {
   static constexpr int ROW = D * (int)sizeof(T);
-  static constexpr int S1 = sizeof(T) == 2 ? ROW + 64 : ROW;
-  static constexpr int S4 = sizeof(T) == 2 ? 4 * S1 + 16 : 4 * ROW;
+  static constexpr int S1 = sizeof(T) == 2 ? ROW + (DUAL ? 64 : 16) : ROW;
+  static constexpr int S4 = sizeof(T) == 2 && DUAL ? 4 * S1 + 16 : 4 * S1;
   static constexpr int bytes(int rows) { return (rows / 4) * S4; }
   // byte offset of a row; linear in (row / 4, row % 4), so off(a + b) =
   // off(a) + off(b) whenever a is a multiple of 4
   __device__ static constexpr int off(int row) { return (row >> 2) * S4 + (row & 3) * S1; }
   // frag_row lane base: row lane % 32, 8-element chunk parity lane / 32
   __device__ static int row_base(int lane) { return off(lane & 31) + (lane >> 5) * 8 * (int)sizeof(T); }
-  // frag_col lane base (see frag_col)
+  // frag_col lane base (see frag_col); DUAL tiles only
   __device__ static int col_base(int lane) {
+    static_assert(DUAL, "transposed reads need the DUAL layout");
     const int h = lane >> 5;
     if constexpr (sizeof(T) == 2) {
       const int g = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
@@ -104,17 +108,28 @@ struct Layout {
 // Direct global->LDS staging of ROWS rows of a (N, D) matrix into a tile.
 // Each wave instruction fills 64 consecutive 16-byte LDS chunks; the lanes
 // whose chunk is padding stay idle.  init() precomputes, per lane and per
-// instruction, the source byte offset relative to the tile's first row.
-// Rows >= N read row N - 1 (finite data that the masks discard).
-template <typename T, int ROWS, int D, int NW>
+// instruction, the source byte offset relative to the tile's first row.  The
+// loads are buffer loads whose range is the matrix itself (N * row bytes), so
+// rows >= N of a tail tile read as zeros without any clamping.
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+// The direct-to-LDS builtins live in small helpers: called inline from the
+// class-template members below, clang's host pass dropped the host stubs of
+// some kernel instantiations (an undefined symbol at load time).
+__device__ __forceinline__ void buffer_lds16(__amdgpu_buffer_rsrc_t rsrc, FA_LDS char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void global_lds4(const void* src, FA_LDS char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)lds, 4, 0, 0);
+}
+
+template <typename T, int ROWS, int D, int NW, bool DUAL = true>
 struct Stager {
-  using L = Layout<T, D>;
+  using L = Layout<T, D, DUAL>;
   static constexpr int CS1 = L::S1 / 16, CS4 = L::S4 / 16, CROW = L::ROW / 16;
   static constexpr int NCH = (ROWS / 4) * CS4;
   static constexpr int NINST = (NCH + 63) / 64;
   static constexpr int PER = (NINST + NW - 1) / NW;
-  static constexpr int ROW_SHIFT = __builtin_ctz(L::ROW);
-  static_assert((L::ROW & (L::ROW - 1)) == 0, "row bytes must be a power of two");
   int src[PER];
 
   __device__ void init(int wave, int lane) {
@@ -126,22 +141,15 @@ struct Stager {
     }
   }
 
+  // g: the (N, D) matrix of this (batch, head); N * ROW < 2^31.
   __device__ void issue(FA_LDS char* tile, const T* g, int row0, int N, int wave) const {
-    const char* gb = (const char*)g;
-    const bool whole = row0 + ROWS <= N;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, N * L::ROW, kBufferWord3);
+    const int base = row0 * L::ROW;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int inst = k * NW + wave;
-      if (inst < NINST && src[k] >= 0) {
-        const char* ptr;
-        if (whole) {
-          ptr = gb + (size_t)row0 * L::ROW + src[k];
-        } else {
-          const int r = min(row0 + (src[k] >> ROW_SHIFT), N - 1);
-          ptr = gb + (size_t)r * L::ROW + (src[k] & (L::ROW - 1));
-        }
-        __builtin_amdgcn_global_load_lds(ptr, (FA_LDS void*)(tile + inst * 1024), 16, 0, 0);
-      }
+      if (inst < NINST && src[k] >= 0) buffer_lds16(rsrc, tile + inst * 1024, base + src[k]);
     }
   }
 };
@@ -156,20 +164,32 @@ __device__ __forceinline__ void stage_vec(FA_LDS char* dst, const void* g, int r
   for (int base = 0; base < ROWS; base += 64) {
     if (wave == wave_id && base + lane < ROWS) {
       const int gr = min(row0 + base + lane, N - 1);
-      __builtin_amdgcn_global_load_lds((const char*)g + (size_t)gr * 4,
-                                       (FA_LDS void*)(dst + base * 4), 4, 0, 0);
+      global_lds4((const char*)g + (size_t)gr * 4, dst + base * 4);
     }
   }
 }
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Optional wave priority around MFMA issue phases (build with -DFA_SETPRIO=1):
+// a wave issuing a block of MFMAs is preferred by the SIMD's arbiter over its
+// co-resident wave, which is then left the VALU.
+#ifndef FA_SETPRIO
+#define FA_SETPRIO 0
+#endif
+__device__ __forceinline__ void prio_hi() {
+  if (FA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+}
+__device__ __forceinline__ void prio_lo() {
+  if (FA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+}
+
 // A/B fragment along D: 8 consecutive elements of tile row rb + lane % 32 at
 // column 8 * (2 * ks + lane / 32); rb is a multiple of 4, `base` =
 // Layout::row_base(lane).
-template <typename T, int D>
+template <typename T, int D, bool DUAL = true>
 __device__ __forceinline__ frag_t<T> frag_row(const FA_LDS char* tile, int base, int rb, int ks) {
-  using L = Layout<T, D>;
+  using L = Layout<T, D, DUAL>;
   const FA_LDS char* p = tile + base + L::off(rb) + ks * 16 * (int)sizeof(T);
   if constexpr (sizeof(T) == 2) {
     return *(const FA_LDS bf16x8*)p;

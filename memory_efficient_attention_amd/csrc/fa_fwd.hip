@@ -6,10 +6,10 @@
 // packed rows, block-diagonal by segment id (same README, "Sequence packing";
 // changelog "Added": the PACKED forward variant).
 //
-// One workgroup = 8 waves = 256 queries of one (batch, head).  Each wave owns
-// 32 queries and computes S^T = K Q^T for a 64-key tile (two 32x32 MFMA
-// tiles), so the softmax statistics of a query live in one lane pair (l,
-// l+32).  Q^T stays in registers for the whole key walk; K and V tiles are
+// One workgroup = FWD_WAVES waves of one (batch, head).  Each wave owns
+// FWD_QBW blocks of 32 queries and computes S^T = K Q^T for a 64-key tile
+// (32x32 MFMA tiles), so the softmax statistics of a query live in one lane
+// pair (l, l+32); every K and V^T fragment read from LDS feeds FWD_QBW MFMAs.  Q^T stays in registers for the whole key walk; K and V tiles are
 // double-buffered in LDS with direct global->LDS loads.  O^T += V^T P^T takes
 // P^T straight from the accumulator and V^T from the V tile through the
 // transposing LDS read.  Causal / packed structure is used at wave
@@ -23,13 +23,17 @@
 namespace fa {
 
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) {
-  constexpr int NW = FWD_WAVES, BM = FWD_BM, BN = KEY_TILE;
+__global__ void __launch_bounds__(FWD_WAVES * 64, FA_FWD_WPE) fwd_kernel(const FwdParams p) {
+  constexpr int NW = FWD_WAVES, QBW = FWD_QBW, QW = 32 * QBW, BM = FWD_BM, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
-  using L = Layout<T, D>;
-  using St = Stager<T, BN, D, NW>;
-  constexpr int TILE = L::bytes(BN);
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE + 2 * BN * 4];
+  // K is read only along rows (row-only layout), V only transposed (DUAL).
+  using LK = Layout<T, D, false>;
+  using LV = Layout<T, D, true>;
+  using StK = Stager<T, BN, D, NW, false>;
+  using StV = Stager<T, BN, D, NW, true>;
+  constexpr int TK = LK::bytes(BN), TV = LV::bytes(BN);
+  // layout: K[2] | V[2] | seg[2]
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * TK + 2 * TV + 2 * BN * 4];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -49,11 +53,11 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
   const int32_t* seg = p.seg ? p.seg + (size_t)b * N : nullptr;
   const bool packed = seg != nullptr;
 
+  // The wave owns queries qw0 .. qw0 + QW - 1, in QBW blocks of 32; lane l
+  // holds query qw0 + 32 qb + l % 32 of block qb.
   const int q0 = qt * BM;
-  const int qw0 = q0 + wave * 32;
-  const int qi = qw0 + col;
-  const int qc = min(qi, N - 1);
-  const int qlast = min(qw0 + 31, N - 1);
+  const int qw0 = q0 + wave * QW;
+  const int qlast = min(qw0 + QW - 1, N - 1);
 
   int kt_lo = 0, kt_hi;
   if (packed) {
@@ -64,32 +68,43 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
     kt_hi = ((CAUSAL ? min(q0 + BM, N) : N) - 1) / BN;
   }
 
-  frag_t<T> qf[KS];
+  frag_t<T> qf[QBW][KS];
+  int segq[QBW];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag_row<T, D>(gq, qc, 2 * ks + h);
-  int segq = 0, segq_first = 0, segq_last = 0;
+  for (int qb = 0; qb < QBW; ++qb) {
+    const int qc = min(qw0 + 32 * qb + col, N - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = gfrag_row<T, D>(gq, qc, 2 * ks + h);
+    segq[qb] = packed ? seg[qc] : 0;
+  }
+  int segq_first = 0, segq_last = 0;
   if (packed) {
-    segq = seg[qc];
     segq_first = seg[min(qw0, N - 1)];
     segq_last = seg[qlast];
   }
 
-  St st;
-  st.init(wave, lane);
-  const int rbase = L::row_base(lane);
-  const int cbase = L::col_base(lane);
+  StK stk;
+  StV stv;
+  stk.init(wave, lane);
+  stv.init(wave, lane);
+  const int rbase = LK::row_base(lane);
+  const int cbase = LV::col_base(lane);
 
-  f32x16 oacc[DB];
+  f32x16 oacc[QBW][DB];
+  float msc[QBW], lsum[QBW];   // reference max (times c, log2 units), lane's half of the row sum
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float msc = -INFINITY;   // reference max of the row, times c (log2 units)
-  float lsum = 0.f;        // this lane's half of the row sum, relative to msc
+  for (int qb = 0; qb < QBW; ++qb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
+    msc[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+  }
   const float c = p.c;
 
   auto stage = [&](int kt, int buf) {
-    st.issue(smem + buf * TILE, gk, kt * BN, N, wave);
-    st.issue(smem + (2 + buf) * TILE, gv, kt * BN, N, wave);
-    if (packed) stage_vec<BN>(smem + 4 * TILE + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
+    stk.issue(smem + buf * TK, gk, kt * BN, N, wave);
+    stv.issue(smem + 2 * TK + buf * TV, gv, kt * BN, N, wave);
+    if (packed) stage_vec<BN>(smem + 2 * TK + 2 * TV + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
   };
 
   if (kt_lo <= kt_hi) stage(kt_lo, 0);
@@ -99,9 +114,9 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
     __syncthreads();
     if (kt < kt_hi) stage(kt + 1, buf ^ 1);
 
-    const FA_LDS char* Ks = smem + buf * TILE;
-    const FA_LDS char* Vs = smem + (2 + buf) * TILE;
-    const FA_LDS int* segk = (const FA_LDS int*)(smem + 4 * TILE + buf * BN * 4);
+    const FA_LDS char* Ks = smem + buf * TK;
+    const FA_LDS char* Vs = smem + 2 * TK + buf * TV;
+    const FA_LDS int* segk = (const FA_LDS int*)(smem + 2 * TK + 2 * TV + buf * BN * 4);
     const int k0 = kt * BN;
     const int klast = min(k0 + BN, N) - 1;
 
@@ -117,15 +132,22 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
     }
     if (skip) continue;
 
-    // S^T = K Q^T for the wave's 32 queries.
-    f32x16 sacc[KB];
+    // S^T = K Q^T, key block by key block (so that block 0's softmax can run
+    // under block 1's MFMAs); each K fragment feeds the QBW query blocks.
+    f32x16 sacc[QBW][KB];
+    prio_hi();
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+      for (int qb = 0; qb < QBW; ++qb) sacc[qb][kb] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) mma(sacc[kb], frag_row<T, D>(Ks, rbase, 32 * kb, ks), qf[ks]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const frag_t<T> a = frag_row<T, D, false>(Ks, rbase, 32 * kb, ks);
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) mma(sacc[qb][kb], a, qf[qb][ks]);
+      }
     }
+    prio_lo();
 
     if (!full) {
 #pragma unroll
@@ -135,66 +157,114 @@ __global__ void __launch_bounds__(FWD_WAVES * 64) fwd_kernel(const FwdParams p) 
           const int kr = 32 * kb + 8 * j + 4 * h;
           i32x4 sk = packed ? *(const FA_LDS i32x4*)(segk + kr) : i32x4{0, 0, 0, 0};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = k0 + kr + i;
-            const bool vis = key < N && (!CAUSAL || key <= qi) && (!packed || sk[i] == segq);
-            if (!vis) sacc[kb][4 * j + i] = -INFINITY;
+          for (int qb = 0; qb < QBW; ++qb) {
+            const int qi = qw0 + 32 * qb + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = k0 + kr + i;
+              const bool vis = key < N && (!CAUSAL || key <= qi) && (!packed || sk[i] == segq[qb]);
+              if (!vis) sacc[qb][kb][4 * j + i] = -INFINITY;
+            }
           }
         }
       }
     }
 
-    // Online softmax in base 2 with a lazily moved reference max.  Both lanes
-    // of a pair hold the same query and take the same decisions.
-    float tmax = -INFINITY;
+    // Online softmax in base 2 with a lazily moved reference max.  The
+    // probabilities are computed against the current reference first; only
+    // when some row's max outgrows it by 2^RESCALE_LOG2 (rare) is the
+    // reference moved, O and the sum rescaled, and the tile's probabilities
+    // recomputed.  Both lanes of a pair hold the same query and take the same
+    // decisions; row max and row sum run as 4 independent chains.
+    float ptile[QBW][KB][16];
+    float ls[QBW][4];
+    bool grow[QBW];
+    float tsc[QBW];
+    bool any_grow = false;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int qb = 0; qb < QBW; ++qb) {
+      const float mref = (msc[qb] == -INFINITY) ? 0.f : msc[qb];
+      float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
-    tmax = fmaxf(tmax, other_half(tmax));
-    const float tsc = tmax * c;
-    const bool grow = tsc > msc + RESCALE_LOG2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      // alpha is 1 for rows that keep their reference (also when it is still
-      // -inf: no visible key yet), and 0 for a row's first visible tile.
-      const float alpha = grow ? exp2_fast(msc - tsc) : 1.f;
-      msc = grow ? tsc : msc;
-      lsum *= alpha;
+      for (int r = 0; r < 4; ++r) ls[qb][r] = 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          const float sv = sacc[qb][kb][r];
+          tm[r & 3] = fmaxf(tm[r & 3], sv);
+          const float e = exp2_fast(fmaf(sv, c, -mref));
+          ptile[qb][kb][r] = e;
+          ls[qb][r & 3] += e;
+        }
+      float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+      tmax = fmaxf(tmax, other_half(tmax));
+      tsc[qb] = tmax * c;
+      grow[qb] = tsc[qb] > msc[qb] + RESCALE_LOG2;
+      any_grow = any_grow || grow[qb];
     }
-    const float mref = (msc == -INFINITY) ? 0.f : msc;
+    if (__builtin_amdgcn_ballot_w64(any_grow) != 0) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int qb = 0; qb < QBW; ++qb) {
+        // alpha is 1 for rows that keep their reference (also when it is
+        // still -inf: no visible key yet), 0 for a row's first visible tile.
+        const float alpha = grow[qb] ? exp2_fast(msc[qb] - tsc[qb]) : 1.f;
+        msc[qb] = grow[qb] ? tsc[qb] : msc[qb];
+        lsum[qb] *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = exp2_fast(fmaf(sacc[kb][r], c, -mref));
-        sacc[kb][r] = e;
-        lsum += e;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+        const float mref = (msc[qb] == -INFINITY) ? 0.f : msc[qb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ls[qb][r] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = exp2_fast(fmaf(sacc[qb][kb][r], c, -mref));
+            ptile[qb][kb][r] = e;
+            ls[qb][r & 3] += e;
+          }
       }
-
-    // O^T += V^T P^T.
-    frag_t<T> pf[KB][2];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      pf[kb][0] = acc_frag<T>(sacc[kb], 0);
-      pf[kb][1] = acc_frag<T>(sacc[kb], 1);
     }
+    frag_t<T> pf[QBW][KB][2];
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      lsum[qb] += (ls[qb][0] + ls[qb][1]) + (ls[qb][2] + ls[qb][3]);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x16 e;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = ptile[qb][kb][r];
+        pf[qb][kb][0] = acc_frag<T>(e, 0);
+        pf[qb][kb][1] = acc_frag<T>(e, 1);
+      }
+    }
+
+    // O^T += V^T P^T: each V^T fragment feeds the QBW query blocks.
+    prio_hi();
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-          mma(oacc[db], frag_col<T, D>(Vs, cbase, 32 * kb + 16 * kc, 32 * db), pf[kb][kc]);
+        for (int kc = 0; kc < 2; ++kc) {
+          const frag_t<T> a = frag_col<T, D>(Vs, cbase, 32 * kb + 16 * kc, 32 * db);
+#pragma unroll
+          for (int qb = 0; qb < QBW; ++qb) mma(oacc[qb][db], a, pf[qb][kb][kc]);
+        }
+    prio_lo();
   }
 
-  const float lt = lsum + other_half(lsum);
-  if (qi < N) {
-    store_rows<T, D>((T*)p.o + off, qi, oacc, 1.f / lt, lane);
-    if (h == 0) p.lse[(size_t)bh * N + qi] = (msc + log2_fast(lt)) * kLn2;
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    const float lt = lsum[qb] + other_half(lsum[qb]);
+    const int qi = qw0 + 32 * qb + col;
+    if (qi < N) {
+      store_rows<T, D>((T*)p.o + off, qi, oacc[qb], 1.f / lt, lane);
+      if (h == 0) p.lse[(size_t)bh * N + qi] = (msc[qb] + log2_fast(lt)) * kLn2;
+    }
   }
 }
 

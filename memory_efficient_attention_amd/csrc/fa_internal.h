@@ -7,12 +7,20 @@
 
 namespace fa {
 
-// Tile sizes.  Forward and dQ: one workgroup owns FWD_WAVES * 32 queries and
-// walks key tiles of KEY_TILE keys.  dK/dV: one workgroup owns DKV_WAVES * 32
-// keys and walks query tiles of QRY_TILE queries.
-// (Each can be overridden at build time with -DFA_<NAME>=value for tuning.)
+// Tile sizes.  Forward: one workgroup owns FWD_WAVES waves x FWD_QBW blocks
+// of 32 queries and walks key tiles of KEY_TILE keys; each K / V fragment
+// read from LDS feeds FWD_QBW MFMAs.  dQ: DQ_WAVES waves x 32 queries, same
+// key tiles.  dK/dV: DKV_WAVES waves x 32 keys, walking query tiles of
+// QRY_TILE queries.  Each can be overridden at build time with
+// -DFA_<NAME>=value for tuning.
 #ifndef FA_FWD_WAVES
 #define FA_FWD_WAVES 8
+#endif
+#ifndef FA_FWD_QBW
+#define FA_FWD_QBW 1
+#endif
+#ifndef FA_DQ_WAVES
+#define FA_DQ_WAVES 8
 #endif
 #ifndef FA_KEY_TILE
 #define FA_KEY_TILE 64
@@ -23,8 +31,20 @@ namespace fa {
 #ifndef FA_QRY_TILE
 #define FA_QRY_TILE 32
 #endif
+// Waves per SIMD each kernel is compiled for (its register budget is 512 /
+// this): the register-blocked forward needs one wave per SIMD, dQ and dK/dV
+// run two.
+#ifndef FA_FWD_WPE
+#define FA_FWD_WPE (FA_FWD_QBW > 1 ? 1 : 2)
+#endif
+#ifndef FA_WAVES_PER_EU
+#define FA_WAVES_PER_EU 2
+#endif
 constexpr int FWD_WAVES = FA_FWD_WAVES;
-constexpr int FWD_BM = FWD_WAVES * 32;
+constexpr int FWD_QBW = FA_FWD_QBW;
+constexpr int FWD_BM = FWD_WAVES * 32 * FWD_QBW;
+constexpr int DQ_WAVES = FA_DQ_WAVES;
+constexpr int DQ_BM = DQ_WAVES * 32;
 constexpr int KEY_TILE = FA_KEY_TILE;
 constexpr int DKV_WAVES = FA_DKV_WAVES;
 constexpr int DKV_BN = DKV_WAVES * 32;
