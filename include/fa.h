@@ -77,7 +77,8 @@ typedef enum fa_dtype {
 /*
  * Bytes of workspace fa_fwd (for_bwd = 0) or fa_bwd (for_bwd = 1) needs for
  * this shape.  O(B*H*N): 256 bytes of flags, plus for the backward two fp32
- * (B, H, N) arrays (the row sums D_i = dO_i . O_i and log2-domain LSE), plus
+ * (B, H, N) arrays (the row sums D_i = dO_i . O_i, stored negated, and the
+ * log2-domain LSE), plus
  * with has_seg two per-tile range tables of B * ceil(N/32) int32 pairs.
  * Returns 0 for shapes fa_fwd / fa_bwd would refuse.
  */

@@ -19,7 +19,8 @@
 namespace fa {
 
 // ---------------------------------------------------------------- preprocess
-// delta[r] = sum_d dO[r, d] * O[r, d] (O as stored), lse2[r] = lse[r] * log2(e).
+// delta[r] = -sum_d dO[r, d] * O[r, d] (O as stored; kept negated so the
+// consumers add it, or start an accumulator from it), lse2[r] = lse[r] * log2(e).
 // LPR lanes share one row, each reading 16 contiguous bytes of O and dO.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
@@ -46,7 +47,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
 #pragma unroll
   for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
   if (row < p.rows && sub == 0) {
-    p.delta[row] = acc;
+    p.delta[row] = -acc;
     p.lse2[row] = p.lse[row] * kLog2e;
   }
 }
@@ -111,7 +112,7 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, FA_WAVES_PER_EU) dq_kernel(cons
     dof[ks] = gfrag_row<T, D>(gdo, qc, 2 * ks + h);
   }
   const float lse2 = p.lse2[(size_t)bh * N + qc];
-  const float dlt = p.delta[(size_t)bh * N + qc];
+  const float ndlt = p.delta[(size_t)bh * N + qc];   // -D_i
   int segq = 0, segq_first = 0, segq_last = 0;
   if (packed) {
     segq = seg[qc];
@@ -191,7 +192,7 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, FA_WAVES_PER_EU) dq_kernel(cons
             if (!vis) s = -INFINITY;
           }
           const float pv = exp2_fast(fmaf(s, c, -lse2));
-          sacc[kb][4 * j + i] = pv * (dpacc[kb][4 * j + i] - dlt);
+          sacc[kb][4 * j + i] = pv * (dpacc[kb][4 * j + i] + ndlt);
         }
       }
     }
@@ -329,17 +330,30 @@ __global__ void __launch_bounds__(DKV_WAVES * 64, FA_WAVES_PER_EU) dkdv_kernel(c
     }
     if (skip) continue;
 
-    // Visibility bits of this lane's 16 accumulator elements per query block
-    // (bit 4j + i: query 32qb + 8j + 4h + i of the tile, key kj).  Computed
-    // before the products so that the tile's MFMA / VALU work below is one
-    // branch-free region the scheduler can interleave.
-    uint32_t vis[QB];
+    // S = Q K^T and dP - D = dO V^T - D, block by block: the dP accumulator
+    // starts from -D_i (stored negated by the preprocess), so the MFMAs
+    // deliver dP - D directly.
+    f32x16 sacc[QB], dpacc[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) vis[qb] = 0xFFFFu;
+    for (int qb = 0; qb < QB; ++qb) {
+      sacc[qb] = f32x16{};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 nd = *(const FA_LDS f32x4*)(dls + 32 * qb + 8 * j + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dpacc[qb][4 * j + i] = nd[i];
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        mma(sacc[qb], frag_row<T, D>(Qs, rbase, 32 * qb, ks), kf[ks]);
+        mma(dpacc[qb], frag_row<T, D>(dOs, rbase, 32 * qb, ks), vf[ks]);
+      }
+    }
+
     if (!full) {
+      // accumulator element 4j + i of block qb: query 32qb + 8j + 4h + i, key kj
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        uint32_t bits = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int qr = 32 * qb + 8 * j + 4 * h;
@@ -348,42 +362,24 @@ __global__ void __launch_bounds__(DKV_WAVES * 64, FA_WAVES_PER_EU) dkdv_kernel(c
           for (int i = 0; i < 4; ++i) {
             const int q = q0 + qr + i;
             const bool v = q < N && kj < N && (!CAUSAL || kj <= q) && (!packed || sq[i] == segk);
-            bits |= (v ? 1u : 0u) << (4 * j + i);
+            if (!v) sacc[qb][4 * j + i] = -INFINITY;
           }
         }
-        vis[qb] = bits;
       }
     }
 
-    // S = Q K^T and dP = dO V^T, block by block.
-    f32x16 sacc[QB], dpacc[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      sacc[qb] = f32x16{};
-      dpacc[qb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        mma(sacc[qb], frag_row<T, D>(Qs, rbase, 32 * qb, ks), kf[ks]);
-        mma(dpacc[qb], frag_row<T, D>(dOs, rbase, 32 * qb, ks), vf[ks]);
-      }
-    }
-
-    // Per block: P = exp2(S c - lse2), dS = P (dP - D_i); then dV^T += dO^T P
-    // and dK^T += Q^T dS.  Block qb's VALU work can run under block qb+1's
-    // MFMAs.
+    // Per block: P = exp2(S c - lse2), dS = P (dP - D); then dV^T += dO^T P
+    // and dK^T += Q^T dS.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int qr = 32 * qb + 8 * j + 4 * h;
-        const f32x4 l2 = *(const FA_LDS f32x4*)(l2s + qr);
-        const f32x4 dl = *(const FA_LDS f32x4*)(dls + qr);
+        const f32x4 l2 = *(const FA_LDS f32x4*)(l2s + 32 * qb + 8 * j + 4 * h);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float sv = ((vis[qb] >> (4 * j + i)) & 1u) ? sacc[qb][4 * j + i] : -INFINITY;
-          const float pv = exp2_fast(fmaf(sv, c, -l2[i]));
+          const float pv = exp2_fast(fmaf(sacc[qb][4 * j + i], c, -l2[i]));
           sacc[qb][4 * j + i] = pv;
-          dpacc[qb][4 * j + i] = pv * (dpacc[qb][4 * j + i] - dl[i]);
+          dpacc[qb][4 * j + i] = pv * dpacc[qb][4 * j + i];
         }
       }
       frag_t<T> pf[2], dsf[2];

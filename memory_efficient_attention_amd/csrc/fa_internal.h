@@ -77,7 +77,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   const float* lse2;     // log2-domain LSE (B, H, N)
-  const float* delta;    // D_i = dO_i . O_i (B, H, N)
+  const float* delta;    // -D_i = -dO_i . O_i (B, H, N)
   const int32_t* seg;
   const int2* tab;       // dQ: per query tile key-tile range; dK/dV: per key tile query-tile range
   int B, H, N, ntiles;
