@@ -134,16 +134,18 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   p.B = B;
   p.H = H;
   p.N = N;
-  p.nqt = (N + fa::FWD_BM - 1) / fa::FWD_BM;
+  const int nw = fa::waves_for(seg != nullptr);
+  const int bm = nw * 32;   // queries per workgroup
+  p.nqt = (N + bm - 1) / bm;
   p.scale = scale;
   p.c = log2e_scale(scale);
   if (seg) {
     if (fa::launch_seg_check(seg, B, N, (int32_t*)(w + L.flag), s) != hipSuccess) return FA_ERR_HIP;
-    if (fa::launch_qtile_table(seg, B, N, fa::FWD_BM, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
+    if (fa::launch_qtile_table(seg, B, N, bm, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
         hipSuccess)
       return FA_ERR_HIP;
   }
-  if (fa::launch_fwd(p, dt, D, causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_fwd(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 
@@ -175,12 +177,14 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   float* delta = (float*)(w + L.delta);
   float* lse2 = (float*)(w + L.lse2);
 
+  const int nw = fa::waves_for(seg != nullptr);
+  const int bt = nw * 32;   // queries (dQ) or keys (dK/dV) per workgroup
   if (seg) {
     if (fa::launch_seg_check(seg, B, N, (int32_t*)(w + L.flag), s) != hipSuccess) return FA_ERR_HIP;
-    if (fa::launch_qtile_table(seg, B, N, fa::DQ_BM, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
+    if (fa::launch_qtile_table(seg, B, N, bt, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
         hipSuccess)
       return FA_ERR_HIP;
-    if (fa::launch_ktile_table(seg, B, N, fa::DKV_BN, fa::QRY_TILE, causal != 0, (int2*)(w + L.ktab), s) !=
+    if (fa::launch_ktile_table(seg, B, N, bt, fa::QRY_TILE, causal != 0, (int2*)(w + L.ktab), s) !=
         hipSuccess)
       return FA_ERR_HIP;
   }
@@ -214,13 +218,13 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
 
   if (!record(events, 1, s)) return FA_ERR_HIP;
   p.tab = seg ? (const int2*)(w + L.ktab) : nullptr;
-  p.ntiles = (N + fa::DKV_BN - 1) / fa::DKV_BN;
-  if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  p.ntiles = (N + bt - 1) / bt;
+  if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
 
   if (!record(events, 2, s)) return FA_ERR_HIP;
   p.tab = seg ? (const int2*)(w + L.qtab) : nullptr;
-  p.ntiles = (N + fa::DQ_BM - 1) / fa::DQ_BM;
-  if (fa::launch_bwd_dq(p, dt, D, causal != 0, s) != hipSuccess) return FA_ERR_HIP;
+  p.ntiles = (N + bt - 1) / bt;
+  if (fa::launch_bwd_dq(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
   if (!record(events, 3, s)) return FA_ERR_HIP;
   return FA_OK;
 }

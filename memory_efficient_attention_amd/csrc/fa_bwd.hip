@@ -53,13 +53,13 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
-// One workgroup = 4 waves x 32 queries; walks the key tiles the query tile can
+// One workgroup = NW waves x 32 queries; walks the key tiles the query tile can
 // see.  Per tile: S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T held in registers),
 // P^T and dS^T in registers, dQ^T += K^T dS^T with K^T through the transposing
 // LDS read of the K tile.
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(DQ_WAVES * 64, FA_WAVES_PER_EU) dq_kernel(const BwdParams p) {
-  constexpr int NW = DQ_WAVES, BM = DQ_BM, BN = KEY_TILE;
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdParams p) {
+  constexpr int BM = NW * 32, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
   // K is read along rows and transposed (DUAL), V only along rows.
   using LK = Layout<T, D, true>;
@@ -67,8 +67,11 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, FA_WAVES_PER_EU) dq_kernel(cons
   using StK = Stager<T, BN, D, NW, true>;
   using StV = Stager<T, BN, D, NW, false>;
   constexpr int TK = LK::bytes(BN), TV = LV::bytes(BN);
-  // layout: K[2] | V[2] | seg[2]
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * TK + 2 * TV + 2 * BN * 4];
+  constexpr int S = sizeof(T) == 2 ? stages_for(FA_DQ_STAGES, TK + TV + BN * 4, NW) : 2;
+  static_assert(S >= 2, "two K/V stages must fit in LDS");
+  constexpr int LPT = (StK::NINST + StV::NINST) / NW;
+  // layout: K[S] | V[S] | seg[S]
+  __shared__ __attribute__((aligned(1024))) char smem_raw[S * (TK + TV + BN * 4)];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -124,7 +127,7 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, FA_WAVES_PER_EU) dq_kernel(cons
   StK stk;
   StV stv;
   stk.init(wave, lane);
-  stv.init(wave, lane);
+  stv.init(wave, lane, StK::NINST);
   const int kbase_r = LK::row_base(lane);
   const int vbase_r = LV::row_base(lane);
   const int cbase = LK::col_base(lane);
@@ -134,21 +137,34 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, FA_WAVES_PER_EU) dq_kernel(cons
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
 
   auto stage = [&](int kt, int buf) {
-    stk.issue(smem + buf * TK, gk, kt * BN, N, wave);
-    stv.issue(smem + 2 * TK + buf * TV, gv, kt * BN, N, wave);
-    if (packed) stage_vec<BN>(smem + 2 * TK + 2 * TV + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
+    stk.issue(smem + buf * TK, gk, kt * BN, N);
+    stv.issue(smem + S * TK + buf * TV, gv, kt * BN, N);
+    if (packed) stage_vec<BN>(smem + S * (TK + TV) + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
   };
 
-  if (kt_lo <= kt_hi) stage(kt_lo, 0);
+  // Ring of S stages, as in the forward.
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i)
+    if (kt_lo + i <= kt_hi) stage(kt_lo + i, i);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    settle(qf[ks]);
+    settle(dof[ks]);
+  }
+  settle(lse2);
+  settle(ndlt);
+  settle(segq);
+  settle(segq_first);
+  settle(segq_last);
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int buf = (kt - kt_lo) & 1;
-    wait_loads();
+    const int buf = (kt - kt_lo) % S;
+    wait_tiles<LPT, S - 2>(kt_hi - kt);
     __syncthreads();
-    if (kt < kt_hi) stage(kt + 1, buf ^ 1);
+    if (kt + S - 1 <= kt_hi) stage(kt + S - 1, buf == 0 ? S - 1 : buf - 1);
 
     const FA_LDS char* Ks = smem + buf * TK;
-    const FA_LDS char* Vs = smem + 2 * TK + buf * TV;
-    const FA_LDS int* segk = (const FA_LDS int*)(smem + 2 * TK + 2 * TV + buf * BN * 4);
+    const FA_LDS char* Vs = smem + S * TK + buf * TV;
+    const FA_LDS int* segk = (const FA_LDS int*)(smem + S * (TK + TV) + buf * BN * 4);
     const int k0 = kt * BN;
     const int klast = min(k0 + BN, N) - 1;
 
@@ -216,22 +232,25 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, FA_WAVES_PER_EU) dq_kernel(cons
 }
 
 // ---------------------------------------------------------------- dK / dV
-// One workgroup = 4 waves x 32 keys; walks the query tiles that can see the
+// One workgroup = NW waves x 32 keys; walks the query tiles that can see the
 // key tile.  Per tile: S = Q K^T and dP = dO V^T (K^T, V^T held in registers;
 // the accumulator columns are keys, rows queries), P and dS in registers,
 // dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T through the transposing
 // LDS read.
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(DKV_WAVES * 64, FA_WAVES_PER_EU) dkdv_kernel(const BwdParams p) {
-  constexpr int NW = DKV_WAVES, BNK = DKV_BN, BMQ = QRY_TILE;
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const BwdParams p) {
+  constexpr int BNK = NW * 32, BMQ = QRY_TILE;
   constexpr int KS = D / 16, DB = D / 32, QB = BMQ / 32;
   using L = Layout<T, D>;
   using St = Stager<T, BMQ, D, NW>;
   constexpr int TILE = L::bytes(BMQ);
   constexpr int VEC = BMQ * 4;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE + 6 * VEC];
+  constexpr int S = sizeof(T) == 2 ? stages_for(FA_DKV_STAGES, 2 * TILE + 3 * VEC, NW) : 2;
+  static_assert(S >= 2, "two Q/dO stages must fit in LDS");
+  constexpr int LPT = 2 * St::NINST / NW;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[S * (2 * TILE + 3 * VEC)];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
-  // layout: Q[2] | dO[2] | lse2[2] | delta[2] | seg[2]
+  // layout: Q[S] | dO[S] | lse2[S] | delta[S] | seg[S]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -284,8 +303,9 @@ __global__ void __launch_bounds__(DKV_WAVES * 64, FA_WAVES_PER_EU) dkdv_kernel(c
   }
   const float c = p.c;
 
-  St st;
-  st.init(wave, lane);
+  St stq, stdo;
+  stq.init(wave, lane);
+  stdo.init(wave, lane, St::NINST);
   const int rbase = L::row_base(lane);
   const int cbase = L::col_base(lane);
 
@@ -298,25 +318,36 @@ __global__ void __launch_bounds__(DKV_WAVES * 64, FA_WAVES_PER_EU) dkdv_kernel(c
 
   auto stage = [&](int qt, int buf) {
     const int r0 = qt * BMQ;
-    st.issue(smem + buf * TILE, gq, r0, N, wave);
-    st.issue(smem + (2 + buf) * TILE, gdo, r0, N, wave);
-    stage_vec<BMQ>(smem + 4 * TILE + buf * VEC, glse2, r0, N, wave, 0, lane);
-    stage_vec<BMQ>(smem + 4 * TILE + (2 + buf) * VEC, gdelta, r0, N, wave, 1 % NW, lane);
-    if (packed) stage_vec<BMQ>(smem + 4 * TILE + (4 + buf) * VEC, seg, r0, N, wave, 2 % NW, lane);
+    stq.issue(smem + buf * TILE, gq, r0, N);
+    stdo.issue(smem + (S + buf) * TILE, gdo, r0, N);
+    stage_vec<BMQ>(smem + 2 * S * TILE + buf * VEC, glse2, r0, N, wave, 0, lane);
+    stage_vec<BMQ>(smem + 2 * S * TILE + (S + buf) * VEC, gdelta, r0, N, wave, 1 % NW, lane);
+    if (packed) stage_vec<BMQ>(smem + 2 * S * TILE + (2 * S + buf) * VEC, seg, r0, N, wave, 2 % NW, lane);
   };
 
-  if (qt_lo <= qt_hi) stage(qt_lo, 0);
+  // Ring of S stages, as in the forward.
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i)
+    if (qt_lo + i <= qt_hi) stage(qt_lo + i, i);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    settle(kf[ks]);
+    settle(vf[ks]);
+  }
+  settle(segk);
+  settle(segk_first);
+  settle(segk_last);
   for (int qt = qt_lo; qt <= qt_hi; ++qt) {
-    const int buf = (qt - qt_lo) & 1;
-    wait_loads();
+    const int buf = (qt - qt_lo) % S;
+    wait_tiles<LPT, S - 2>(qt_hi - qt);
     __syncthreads();
-    if (qt < qt_hi) stage(qt + 1, buf ^ 1);
+    if (qt + S - 1 <= qt_hi) stage(qt + S - 1, buf == 0 ? S - 1 : buf - 1);
 
     const FA_LDS char* Qs = smem + buf * TILE;
-    const FA_LDS char* dOs = smem + (2 + buf) * TILE;
-    const FA_LDS float* l2s = (const FA_LDS float*)(smem + 4 * TILE + buf * VEC);
-    const FA_LDS float* dls = (const FA_LDS float*)(smem + 4 * TILE + (2 + buf) * VEC);
-    const FA_LDS int* sqs = (const FA_LDS int*)(smem + 4 * TILE + (4 + buf) * VEC);
+    const FA_LDS char* dOs = smem + (S + buf) * TILE;
+    const FA_LDS float* l2s = (const FA_LDS float*)(smem + 2 * S * TILE + buf * VEC);
+    const FA_LDS float* dls = (const FA_LDS float*)(smem + 2 * S * TILE + (S + buf) * VEC);
+    const FA_LDS int* sqs = (const FA_LDS int*)(smem + 2 * S * TILE + (2 * S + buf) * VEC);
     const int q0 = qt * BMQ;
     const int qlast = min(q0 + BMQ, N) - 1;
 
@@ -419,36 +450,26 @@ hipError_t launch_bwd_pre(const PreParams& p, int dtype, int D, hipStream_t s) {
   return D == 128 ? launch_pre_t<float, 128>(p, s) : launch_pre_t<float, 64>(p, s);
 }
 
-template <typename T, int D, bool CAUSAL>
-static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
-  const long long total = (long long)p.B * p.H * p.ntiles;
-  hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL>), dim3((unsigned)total), dim3(DQ_WAVES * 64), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s) {
+  return dispatch(dtype, D, causal, nw, [&](auto t, auto d, auto c, auto w) {
+    using T = typename decltype(t)::type;
+    constexpr int DD = decltype(d)::value, NW = decltype(w)::value;
+    constexpr bool C = decltype(c)::value;
+    const long long total = (long long)p.B * p.H * p.ntiles;
+    hipLaunchKernelGGL((dq_kernel<T, DD, C, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    return hipGetLastError();
+  });
 }
 
-template <typename T, int D, bool CAUSAL>
-static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t s) {
-  const long long total = (long long)p.B * p.H * p.ntiles;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)total), dim3(DKV_WAVES * 64), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, hipStream_t s) {
-  if (dtype == 0) {
-    if (D == 128) return causal ? launch_dq_t<bf16, 128, true>(p, s) : launch_dq_t<bf16, 128, false>(p, s);
-    return causal ? launch_dq_t<bf16, 64, true>(p, s) : launch_dq_t<bf16, 64, false>(p, s);
-  }
-  if (D == 128) return causal ? launch_dq_t<float, 128, true>(p, s) : launch_dq_t<float, 128, false>(p, s);
-  return causal ? launch_dq_t<float, 64, true>(p, s) : launch_dq_t<float, 64, false>(p, s);
-}
-
-hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, hipStream_t s) {
-  if (dtype == 0) {
-    if (D == 128) return causal ? launch_dkdv_t<bf16, 128, true>(p, s) : launch_dkdv_t<bf16, 128, false>(p, s);
-    return causal ? launch_dkdv_t<bf16, 64, true>(p, s) : launch_dkdv_t<bf16, 64, false>(p, s);
-  }
-  if (D == 128) return causal ? launch_dkdv_t<float, 128, true>(p, s) : launch_dkdv_t<float, 128, false>(p, s);
-  return causal ? launch_dkdv_t<float, 64, true>(p, s) : launch_dkdv_t<float, 64, false>(p, s);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s) {
+  return dispatch(dtype, D, causal, nw, [&](auto t, auto d, auto c, auto w) {
+    using T = typename decltype(t)::type;
+    constexpr int DD = decltype(d)::value, NW = decltype(w)::value;
+    constexpr bool C = decltype(c)::value;
+    const long long total = (long long)p.B * p.H * p.ntiles;
+    hipLaunchKernelGGL((dkdv_kernel<T, DD, C, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace fa

@@ -111,16 +111,31 @@ struct Layout {
 // instruction, the source byte offset relative to the tile's first row.  The
 // loads are buffer loads whose range is the matrix itself (N * row bytes), so
 // rows >= N of a tail tile read as zeros without any clamping.
-constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
-
-// The direct-to-LDS builtins live in small helpers: called inline from the
-// class-template members below, clang's host pass dropped the host stubs of
-// some kernel instantiations (an undefined symbol at load time).
-__device__ __forceinline__ void buffer_lds16(__amdgpu_buffer_rsrc_t rsrc, FA_LDS char* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds, 16, voff, 0, 0, 0);
+//
+// The direct-to-LDS loads are issued from inline assembly.  Issued through
+// the compiler builtins, they make the compiler wait for every outstanding
+// LDS load before each transposing LDS read (it cannot tell which buffer the
+// read touches), which serialises the next tile's loads with the current
+// tile's math.  The kernels instead wait explicitly: s_waitcnt vmcnt(n) with
+// n = the loads issued for the tiles still in flight behind the one needed,
+// then a workgroup barrier.  Hidden from the compiler, these loads can only
+// make its own vmcnt waits (for register loads) stricter, never looser.
+// M0 carries the LDS address; nothing else in these kernels keeps a value in
+// M0 (checked on the built code).  The compiler cannot see the hazards of
+// these instructions, so each waits 5 states after its M0 write, which also
+// covers an SGPR operand (descriptor, address) just written by a VALU op.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* g, int bytes) {
+  const unsigned long long a = (unsigned long long)g;
+  // raw buffer: base, stride 0, num_records = bytes, 32-bit data format
+  return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, 0x00020000};
+}
+__device__ __forceinline__ void buffer_lds16(i32x4 rsrc, FA_LDS char* lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"((unsigned)(size_t)lds), "v"(voff), "s"(rsrc) : "memory");
 }
 __device__ __forceinline__ void global_lds4(const void* src, FA_LDS char* lds) {
-  __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)lds, 4, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dword %1, off"
+               :: "s"((unsigned)(size_t)lds), "v"(src) : "memory");
 }
 
 template <typename T, int ROWS, int D, int NW, bool DUAL = true>
@@ -131,24 +146,43 @@ struct Stager {
   static constexpr int NINST = (NCH + 63) / 64;
   static constexpr int PER = (NINST + NW - 1) / NW;
   int src[PER];
+  int rank;   // this wave's position in the round-robin deal of instructions
 
-  __device__ void init(int wave, int lane) {
+  static constexpr bool lane_active(int P) {
+    return P < NCH && (P % CS4) / CS1 < 4 && (P % CS4) % CS1 < CROW;
+  }
+  // Every instruction has an active lane, so no wave ever skips one of its
+  // loads (the explicit vmcnt waits count them).
+  static constexpr bool every_inst_active() {
+    for (int inst = 0; inst < NINST; ++inst) {
+      bool any = false;
+      for (int lane = 0; lane < 64; ++lane) any = any || lane_active(inst * 64 + lane);
+      if (!any) return false;
+    }
+    return true;
+  }
+  static_assert(every_inst_active(), "a staging instruction would have no active lane");
+
+  // Instruction i goes to wave (first + i) % NW.  Stagers of one tile that
+  // start where the previous one ended deal their instructions round-robin as
+  // a single set, so every wave issues at least floor(total / NW) of them.
+  __device__ void init(int wave, int lane, int first = 0) {
+    rank = (wave - first % NW + NW) % NW;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int P = (k * NW + wave) * 64 + lane;
+      const int P = (k * NW + rank) * 64 + lane;
       const int g = P / CS4, w = P % CS4, b = w / CS1, c = w % CS1;
-      src[k] = (P < NCH && b < 4 && c < CROW) ? ((4 * g + b) * L::ROW + c * 16) : -1;
+      src[k] = lane_active(P) ? ((4 * g + b) * L::ROW + c * 16) : -1;
     }
   }
 
   // g: the (N, D) matrix of this (batch, head); N * ROW < 2^31.
-  __device__ void issue(FA_LDS char* tile, const T* g, int row0, int N, int wave) const {
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, N * L::ROW, kBufferWord3);
+  __device__ void issue(FA_LDS char* tile, const T* g, int row0, int N) const {
+    const i32x4 rsrc = buffer_rsrc(g, N * L::ROW);
     const int base = row0 * L::ROW;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int inst = k * NW + wave;
+      const int inst = k * NW + rank;
       if (inst < NINST && src[k] >= 0) buffer_lds16(rsrc, tile + inst * 1024, base + src[k]);
     }
   }
@@ -169,7 +203,42 @@ __device__ __forceinline__ void stage_vec(FA_LDS char* dst, const void* g, int r
   }
 }
 
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Makes the compiler complete, at this point, the register loads that
+// produced x.  It places its vmcnt waits at first use; a first use inside the
+// tile loop would be re-checked on every iteration with a wait that also
+// drains the staged tiles in flight.
+template <typename X>
+__device__ __forceinline__ void settle(const X& x) {
+  asm volatile("" :: "v"(x));
+}
+__device__ __forceinline__ void settle(const f32x8& x) {
+  settle(f32x4{x[0], x[1], x[2], x[3]});
+  settle(f32x4{x[4], x[5], x[6], x[7]});
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_loads() { wait_vm<0>(); }
+
+// Wait until the loads of the oldest staged tile have landed while `ahead`
+// newer tiles (at most MAXA), PER load instructions each per wave, may still
+// be in flight.  Loads complete in issue order.
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  if constexpr (MAXA >= 3) {
+    if (ahead >= 3) return wait_vm<3 * PER>();
+  }
+  if constexpr (MAXA >= 2) {
+    if (ahead >= 2) return wait_vm<2 * PER>();
+  }
+  if constexpr (MAXA >= 1) {
+    if (ahead >= 1) return wait_vm<PER>();
+  }
+  wait_vm<0>();
+}
 
 // Optional wave priority around MFMA issue phases (build with -DFA_SETPRIO=1):
 // a wave issuing a block of MFMAs is preferred by the SIMD's arbiter over its

@@ -6,25 +6,27 @@
 // packed rows, block-diagonal by segment id (same README, "Sequence packing";
 // changelog "Added": the PACKED forward variant).
 //
-// One workgroup = FWD_WAVES waves of one (batch, head).  Each wave owns
-// FWD_QBW blocks of 32 queries and computes S^T = K Q^T for a 64-key tile
-// (32x32 MFMA tiles), so the softmax statistics of a query live in one lane
-// pair (l, l+32); every K and V^T fragment read from LDS feeds FWD_QBW MFMAs.  Q^T stays in registers for the whole key walk; K and V tiles are
-// double-buffered in LDS with direct global->LDS loads.  O^T += V^T P^T takes
-// P^T straight from the accumulator and V^T from the V tile through the
-// transposing LDS read.  Causal / packed structure is used at wave
-// granularity: key tiles no query of a wave can see are skipped, tiles every
-// query sees fully skip the per-element mask.  The running reference max
-// moves only when a row's max grows by more than 2^RESCALE_LOG2, so the O
-// rescale is a rare, wave-uniform branch.
+// One workgroup = NW waves of one (batch, head).  Each wave owns 32
+// queries and computes S^T = K Q^T for a 64-key tile (32x32 MFMA tiles), so
+// the softmax statistics of a query live in one lane pair (l, l+32).  Q^T
+// stays in registers for the whole key walk; K and V tiles come through a
+// ring of LDS stages filled by direct global->LDS loads.  O^T += V^T P^T
+// takes P^T straight from the accumulator and V^T from the V tile through
+// the transposing LDS read.
+//
+// Causal / packed structure is used at wave granularity: key tiles no query
+// of a wave can see are skipped, tiles every query sees skip the
+// per-element mask.  Probabilities are taken against a per-row reference
+// that moves rarely (see GROW_LIMIT), so the O rescale is a rare,
+// wave-uniform branch.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(FWD_WAVES * 64, FA_FWD_WPE) fwd_kernel(const FwdParams p) {
-  constexpr int NW = FWD_WAVES, QBW = FWD_QBW, QW = 32 * QBW, BM = FWD_BM, BN = KEY_TILE;
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const FwdParams p) {
+  constexpr int BM = NW * 32, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
   // K is read only along rows (row-only layout), V only transposed (DUAL).
   using LK = Layout<T, D, false>;
@@ -32,8 +34,11 @@ __global__ void __launch_bounds__(FWD_WAVES * 64, FA_FWD_WPE) fwd_kernel(const F
   using StK = Stager<T, BN, D, NW, false>;
   using StV = Stager<T, BN, D, NW, true>;
   constexpr int TK = LK::bytes(BN), TV = LV::bytes(BN);
-  // layout: K[2] | V[2] | seg[2]
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * TK + 2 * TV + 2 * BN * 4];
+  constexpr int S = sizeof(T) == 2 ? stages_for(FA_FWD_STAGES, TK + TV + BN * 4, NW) : 2;
+  static_assert(S >= 2, "two K/V stages must fit in LDS");
+  constexpr int LPT = (StK::NINST + StV::NINST) / NW;   // loads per wave per tile, at least
+  // layout: K[S] | V[S] | seg[S]
+  __shared__ __attribute__((aligned(1024))) char smem_raw[S * (TK + TV + BN * 4)];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -53,11 +58,12 @@ __global__ void __launch_bounds__(FWD_WAVES * 64, FA_FWD_WPE) fwd_kernel(const F
   const int32_t* seg = p.seg ? p.seg + (size_t)b * N : nullptr;
   const bool packed = seg != nullptr;
 
-  // The wave owns queries qw0 .. qw0 + QW - 1, in QBW blocks of 32; lane l
-  // holds query qw0 + 32 qb + l % 32 of block qb.
+  // The wave owns queries qw0 .. qw0 + 31; lane l holds query qw0 + l % 32.
   const int q0 = qt * BM;
-  const int qw0 = q0 + wave * QW;
-  const int qlast = min(qw0 + QW - 1, N - 1);
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + col;
+  const int qc = min(qi, N - 1);
+  const int qlast = min(qw0 + 31, N - 1);
 
   int kt_lo = 0, kt_hi;
   if (packed) {
@@ -68,17 +74,12 @@ __global__ void __launch_bounds__(FWD_WAVES * 64, FA_FWD_WPE) fwd_kernel(const F
     kt_hi = ((CAUSAL ? min(q0 + BM, N) : N) - 1) / BN;
   }
 
-  frag_t<T> qf[QBW][KS];
-  int segq[QBW];
+  frag_t<T> qf[KS];
 #pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    const int qc = min(qw0 + 32 * qb + col, N - 1);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = gfrag_row<T, D>(gq, qc, 2 * ks + h);
-    segq[qb] = packed ? seg[qc] : 0;
-  }
-  int segq_first = 0, segq_last = 0;
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag_row<T, D>(gq, qc, 2 * ks + h);
+  int segq = 0, segq_first = 0, segq_last = 0;
   if (packed) {
+    segq = seg[qc];
     segq_first = seg[min(qw0, N - 1)];
     segq_last = seg[qlast];
   }
@@ -86,37 +87,44 @@ __global__ void __launch_bounds__(FWD_WAVES * 64, FA_FWD_WPE) fwd_kernel(const F
   StK stk;
   StV stv;
   stk.init(wave, lane);
-  stv.init(wave, lane);
+  stv.init(wave, lane, StK::NINST);
   const int rbase = LK::row_base(lane);
   const int cbase = LV::col_base(lane);
 
-  f32x16 oacc[QBW][DB];
-  float msc[QBW], lsum[QBW];   // reference max (times c, log2 units), lane's half of the row sum
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
-    msc[qb] = -INFINITY;
-    lsum[qb] = 0.f;
-  }
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  // msc: the row's reference (scores times c, log2 units; -inf until the row
+  // has seen a visible key); lsum: this lane's half of the row sum.
+  float msc = -INFINITY, lsum = 0.f;
   const float c = p.c;
 
   auto stage = [&](int kt, int buf) {
-    stk.issue(smem + buf * TK, gk, kt * BN, N, wave);
-    stv.issue(smem + 2 * TK + buf * TV, gv, kt * BN, N, wave);
-    if (packed) stage_vec<BN>(smem + 2 * TK + 2 * TV + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
+    stk.issue(smem + buf * TK, gk, kt * BN, N);
+    stv.issue(smem + S * TK + buf * TV, gv, kt * BN, N);
+    if (packed) stage_vec<BN>(smem + S * (TK + TV) + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
   };
+  // Ring of S stages: tiles kt + 1 .. kt + S - 2 stay in flight while tile kt
+  // is used; the barrier after the wait also tells every wave that the
+  // buffer of tile kt - 1 is free for tile kt + S - 1.
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i)
+    if (kt_lo + i <= kt_hi) stage(kt_lo + i, i);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+  settle(segq);
+  settle(segq_first);
+  settle(segq_last);
 
-  if (kt_lo <= kt_hi) stage(kt_lo, 0);
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int buf = (kt - kt_lo) & 1;
-    wait_loads();
+    const int buf = (kt - kt_lo) % S;
+    wait_tiles<LPT, S - 2>(kt_hi - kt);
     __syncthreads();
-    if (kt < kt_hi) stage(kt + 1, buf ^ 1);
+    if (kt + S - 1 <= kt_hi) stage(kt + S - 1, buf == 0 ? S - 1 : buf - 1);
 
     const FA_LDS char* Ks = smem + buf * TK;
-    const FA_LDS char* Vs = smem + 2 * TK + buf * TV;
-    const FA_LDS int* segk = (const FA_LDS int*)(smem + 2 * TK + 2 * TV + buf * BN * 4);
+    const FA_LDS char* Vs = smem + S * TK + buf * TV;
+    const FA_LDS int* segk = (const FA_LDS int*)(smem + S * (TK + TV) + buf * BN * 4);
     const int k0 = kt * BN;
     const int klast = min(k0 + BN, N) - 1;
 
@@ -132,156 +140,119 @@ __global__ void __launch_bounds__(FWD_WAVES * 64, FA_FWD_WPE) fwd_kernel(const F
     }
     if (skip) continue;
 
-    // S^T = K Q^T, key block by key block (so that block 0's softmax can run
-    // under block 1's MFMAs); each K fragment feeds the QBW query blocks.
-    f32x16 sacc[QBW][KB];
-    prio_hi();
+    // S^T = K Q^T, one 32-key block per accumulator.
+    f32x16 sacc[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      sacc[kb] = f32x16{};
 #pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) sacc[qb][kb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const frag_t<T> a = frag_row<T, D, false>(Ks, rbase, 32 * kb, ks);
-#pragma unroll
-        for (int qb = 0; qb < QBW; ++qb) mma(sacc[qb][kb], a, qf[qb][ks]);
-      }
+      for (int ks = 0; ks < KS; ++ks) mma(sacc[kb], frag_row<T, D, false>(Ks, rbase, 32 * kb, ks), qf[ks]);
     }
-    prio_lo();
-
     if (!full) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kr = 32 * kb + 8 * j + 4 * h;
-          i32x4 sk = packed ? *(const FA_LDS i32x4*)(segk + kr) : i32x4{0, 0, 0, 0};
+          const i32x4 sk = packed ? *(const FA_LDS i32x4*)(segk + kr) : i32x4{0, 0, 0, 0};
 #pragma unroll
-          for (int qb = 0; qb < QBW; ++qb) {
-            const int qi = qw0 + 32 * qb + col;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = k0 + kr + i;
-              const bool vis = key < N && (!CAUSAL || key <= qi) && (!packed || sk[i] == segq[qb]);
-              if (!vis) sacc[qb][kb][4 * j + i] = -INFINITY;
-            }
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + kr + i;
+            const bool vis = key < N && (!CAUSAL || key <= qi) && (!packed || sk[i] == segq);
+            if (!vis) sacc[kb][4 * j + i] = -INFINITY;
           }
         }
       }
     }
 
-    // Online softmax in base 2 with a lazily moved reference max.  The
-    // probabilities are computed against the current reference first; only
-    // when some row's max outgrows it by 2^RESCALE_LOG2 (rare) is the
-    // reference moved, O and the sum rescaled, and the tile's probabilities
-    // recomputed.  Both lanes of a pair hold the same query and take the same
-    // decisions; row max and row sum run as 4 independent chains.
-    float ptile[QBW][KB][16];
-    float ls[QBW][4];
-    bool grow[QBW];
-    float tsc[QBW];
-    bool any_grow = false;
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      const float mref = (msc[qb] == -INFINITY) ? 0.f : msc[qb];
-      float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ls[qb][r] = 0.f;
+    // Probabilities against the current reference; a row whose partial sum
+    // reaches GROW_LIMIT (an overflow to inf included) or that has no
+    // reference yet sends the wave down the rare path, which moves the
+    // references to the tile's row maxima, rescales O and the sums, and
+    // recomputes the probabilities.  Both lanes of a row see the same row
+    // max, so they take the same decisions.
+    float ptile[KB][16];
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    {
+      const float mref = (msc == -INFINITY) ? 0.f : msc;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float sv = sacc[qb][kb][r];
-          tm[r & 3] = fmaxf(tm[r & 3], sv);
-          const float e = exp2_fast(fmaf(sv, c, -mref));
-          ptile[qb][kb][r] = e;
-          ls[qb][r & 3] += e;
+          const float e = exp2_fast(fmaf(sacc[kb][r], c, -mref));
+          ptile[kb][r] = e;
+          ls[r & 3] += e;
         }
+    }
+    const float lpart = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    const bool trigger = msc == -INFINITY || !(lpart < GROW_LIMIT);
+    if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
+      float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], sacc[kb][r]);
       float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
       tmax = fmaxf(tmax, other_half(tmax));
-      tsc[qb] = tmax * c;
-      grow[qb] = tsc[qb] > msc[qb] + RESCALE_LOG2;
-      any_grow = any_grow || grow[qb];
+      const float tsc = tmax * c;
+      const bool grow = tsc > msc;
+      // alpha is 0 on a row's first visible tile (msc = -inf), 1 if kept.
+      const float alpha = grow ? exp2_fast(msc - tsc) : 1.f;
+      msc = grow ? tsc : msc;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      const float mref = (msc == -INFINITY) ? 0.f : msc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ls[r] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = exp2_fast(fmaf(sacc[kb][r], c, -mref));
+          ptile[kb][r] = e;
+          ls[r & 3] += e;
+        }
     }
-    if (__builtin_amdgcn_ballot_w64(any_grow) != 0) {
+    lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    frag_t<T> pf[KB][2];
 #pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) {
-        // alpha is 1 for rows that keep their reference (also when it is
-        // still -inf: no visible key yet), 0 for a row's first visible tile.
-        const float alpha = grow[qb] ? exp2_fast(msc[qb] - tsc[qb]) : 1.f;
-        msc[qb] = grow[qb] ? tsc[qb] : msc[qb];
-        lsum[qb] *= alpha;
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x16 e;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-        const float mref = (msc[qb] == -INFINITY) ? 0.f : msc[qb];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ls[qb][r] = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = exp2_fast(fmaf(sacc[qb][kb][r], c, -mref));
-            ptile[qb][kb][r] = e;
-            ls[qb][r & 3] += e;
-          }
-      }
-    }
-    frag_t<T> pf[QBW][KB][2];
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      lsum[qb] += (ls[qb][0] + ls[qb][1]) + (ls[qb][2] + ls[qb][3]);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        f32x16 e;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = ptile[qb][kb][r];
-        pf[qb][kb][0] = acc_frag<T>(e, 0);
-        pf[qb][kb][1] = acc_frag<T>(e, 1);
-      }
+      for (int r = 0; r < 16; ++r) e[r] = ptile[kb][r];
+      pf[kb][0] = acc_frag<T>(e, 0);
+      pf[kb][1] = acc_frag<T>(e, 1);
     }
 
-    // O^T += V^T P^T: each V^T fragment feeds the QBW query blocks.
-    prio_hi();
+    // O^T += V^T P^T.
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const frag_t<T> a = frag_col<T, D>(Vs, cbase, 32 * kb + 16 * kc, 32 * db);
-#pragma unroll
-          for (int qb = 0; qb < QBW; ++qb) mma(oacc[qb][db], a, pf[qb][kb][kc]);
-        }
-    prio_lo();
+        for (int kc = 0; kc < 2; ++kc)
+          mma(oacc[db], frag_col<T, D>(Vs, cbase, 32 * kb + 16 * kc, 32 * db), pf[kb][kc]);
   }
 
-#pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    const float lt = lsum[qb] + other_half(lsum[qb]);
-    const int qi = qw0 + 32 * qb + col;
-    if (qi < N) {
-      store_rows<T, D>((T*)p.o + off, qi, oacc[qb], 1.f / lt, lane);
-      if (h == 0) p.lse[(size_t)bh * N + qi] = (msc[qb] + log2_fast(lt)) * kLn2;
-    }
+  const float lt = lsum + other_half(lsum);
+  if (qi < N) {
+    store_rows<T, D>((T*)p.o + off, qi, oacc, 1.f / lt, lane);
+    if (h == 0) p.lse[(size_t)bh * N + qi] = (msc + log2_fast(lt)) * kLn2;
   }
 }
 
-template <typename T, int D, bool CAUSAL>
-static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
-  const long long total = (long long)p.B * p.H * p.nqt;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)total), dim3(FWD_WAVES * 64), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, hipStream_t s) {
-  if (dtype == 0) {
-    if (D == 128) return causal ? launch_fwd_t<bf16, 128, true>(p, s) : launch_fwd_t<bf16, 128, false>(p, s);
-    return causal ? launch_fwd_t<bf16, 64, true>(p, s) : launch_fwd_t<bf16, 64, false>(p, s);
-  }
-  if (D == 128) return causal ? launch_fwd_t<float, 128, true>(p, s) : launch_fwd_t<float, 128, false>(p, s);
-  return causal ? launch_fwd_t<float, 64, true>(p, s) : launch_fwd_t<float, 64, false>(p, s);
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s) {
+  return dispatch(dtype, D, causal, nw, [&](auto t, auto d, auto c, auto w) {
+    using T = typename decltype(t)::type;
+    constexpr int DD = decltype(d)::value, NW = decltype(w)::value;
+    constexpr bool C = decltype(c)::value;
+    const long long total = (long long)p.B * p.H * p.nqt;
+    hipLaunchKernelGGL((fwd_kernel<T, DD, C, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace fa

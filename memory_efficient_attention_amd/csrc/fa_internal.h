@@ -7,53 +7,67 @@
 
 namespace fa {
 
-// Tile sizes.  Forward: one workgroup owns FWD_WAVES waves x FWD_QBW blocks
-// of 32 queries and walks key tiles of KEY_TILE keys; each K / V fragment
-// read from LDS feeds FWD_QBW MFMAs.  dQ: DQ_WAVES waves x 32 queries, same
-// key tiles.  dK/dV: DKV_WAVES waves x 32 keys, walking query tiles of
-// QRY_TILE queries.  Each can be overridden at build time with
-// -DFA_<NAME>=value for tuning.
-#ifndef FA_FWD_WAVES
-#define FA_FWD_WAVES 8
+// Tile sizes.  A workgroup of NW waves owns NW x 32 queries (forward, dQ)
+// or keys (dK/dV); the forward and dQ walk key tiles of KEY_TILE keys, dK/dV
+// walks query tiles of QRY_TILE queries.  Every wave does the same
+// arithmetic in the same order whatever NW is, so the choice of NW never
+// changes a result bit.  Dense (causal or full) calls use WAVES_DENSE waves,
+// whose one staged tile feeds the most waves; packed calls use WAVES_PACKED,
+// whose smaller workgroups track short segments more closely and keep two
+// workgroups per CU in flight.  Overridable at build time
+// (-DFA_<NAME>=value).
+#ifndef FA_WAVES_DENSE
+#define FA_WAVES_DENSE 8
 #endif
-#ifndef FA_FWD_QBW
-#define FA_FWD_QBW 1
-#endif
-#ifndef FA_DQ_WAVES
-#define FA_DQ_WAVES 8
+#ifndef FA_WAVES_PACKED
+#define FA_WAVES_PACKED 4
 #endif
 #ifndef FA_KEY_TILE
 #define FA_KEY_TILE 64
 #endif
-#ifndef FA_DKV_WAVES
-#define FA_DKV_WAVES 8
-#endif
 #ifndef FA_QRY_TILE
 #define FA_QRY_TILE 32
 #endif
-// Waves per SIMD each kernel is compiled for (its register budget is 512 /
-// this): the register-blocked forward needs one wave per SIMD, dQ and dK/dV
-// run two.
-#ifndef FA_FWD_WPE
-#define FA_FWD_WPE (FA_FWD_QBW > 1 ? 1 : 2)
-#endif
+// Waves per SIMD the kernels are compiled for (their register budget is
+// 512 / this per lane).
 #ifndef FA_WAVES_PER_EU
 #define FA_WAVES_PER_EU 2
 #endif
-constexpr int FWD_WAVES = FA_FWD_WAVES;
-constexpr int FWD_QBW = FA_FWD_QBW;
-constexpr int FWD_BM = FWD_WAVES * 32 * FWD_QBW;
-constexpr int DQ_WAVES = FA_DQ_WAVES;
-constexpr int DQ_BM = DQ_WAVES * 32;
+// Load pipeline depth: each kernel keeps up to STAGES - 1 tiles staged ahead
+// of the one it computes on, as far as its LDS share allows.  Measured on
+// MI355X, deeper rings help only dK/dV (whose tiles are half the size); fp32
+// tiles (small shapes only) always use two stages and full waits.
+#ifndef FA_FWD_STAGES
+#define FA_FWD_STAGES 2
+#endif
+#ifndef FA_DQ_STAGES
+#define FA_DQ_STAGES 2
+#endif
+#ifndef FA_DKV_STAGES
+#define FA_DKV_STAGES 4
+#endif
+constexpr int WAVES_DENSE = FA_WAVES_DENSE;
+constexpr int WAVES_PACKED = FA_WAVES_PACKED;
 constexpr int KEY_TILE = FA_KEY_TILE;
-constexpr int DKV_WAVES = FA_DKV_WAVES;
-constexpr int DKV_BN = DKV_WAVES * 32;
 constexpr int QRY_TILE = FA_QRY_TILE;
+constexpr int LDS_PER_CU = 163840;
+constexpr int WAVES_PER_CU = 4 * FA_WAVES_PER_EU;
 
-// Online-softmax reference max: moved only when a row's max exceeds it by
-// more than this many powers of two, so the O accumulator is rescaled rarely;
-// unnormalised probabilities stay below 2^RESCALE_LOG2.
-constexpr float RESCALE_LOG2 = 8.f;
+constexpr int waves_for(bool packed) { return packed ? WAVES_PACKED : WAVES_DENSE; }
+
+// Stages a kernel of NW waves uses: the requested depth, reduced to what
+// fits its share of the CU's LDS (WAVES_PER_CU / NW workgroups share a CU)
+// at `per_stage` bytes per stage (fp32 tiles are twice as large).
+constexpr int stages_for(int requested, int per_stage, int nw) {
+  const int fit = LDS_PER_CU / (WAVES_PER_CU / nw) / per_stage;
+  return requested < fit ? requested : fit;
+}
+
+// Online softmax with a lazily moved reference: probabilities are taken
+// against a per-row reference that moves only when a row's partial sum of
+// unnormalised probabilities in one tile reaches this bound (so every
+// probability stays below it) or the row has no reference yet.
+constexpr float GROW_LIMIT = 65536.f;
 
 struct FwdParams {
   const void* q;
@@ -93,11 +107,29 @@ struct PreParams {
   long long rows;
 };
 
-// Launchers (defined next to their kernels).  dtype: 0 bf16, 1 fp32.
-hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, hipStream_t s);
+// Launchers (defined next to their kernels).  dtype: 0 bf16, 1 fp32; nw:
+// waves per workgroup, WAVES_DENSE or WAVES_PACKED.
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s);
 hipError_t launch_bwd_pre(const PreParams& p, int dtype, int D, hipStream_t s);
-hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, hipStream_t s);
-hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s);
+
+// Calls f(type_c<T>, int_c<D>, bool_c<CAUSAL>, int_c<NW>) for the runtime
+// (dtype, D, causal, nw), so each launcher names its kernel template once.
+template <typename T> struct type_c { using type = T; };
+template <int V> struct int_c { static constexpr int value = V; };
+template <bool V> struct bool_c { static constexpr bool value = V; };
+template <typename F>
+hipError_t dispatch(int dtype, int D, bool causal, int nw, F&& f) {
+  auto by_nw = [&](auto t, auto d, auto c) {
+    return nw == WAVES_PACKED ? f(t, d, c, int_c<WAVES_PACKED>{}) : f(t, d, c, int_c<WAVES_DENSE>{});
+  };
+  auto by_causal = [&](auto t, auto d) {
+    return causal ? by_nw(t, d, bool_c<true>{}) : by_nw(t, d, bool_c<false>{});
+  };
+  auto by_d = [&](auto t) { return D == 128 ? by_causal(t, int_c<128>{}) : by_causal(t, int_c<64>{}); };
+  return dtype == 0 ? by_d(type_c<__bf16>{}) : by_d(type_c<float>{});
+}
 // Per-tile range tables from segment ids (see fa_sched.hip).
 hipError_t launch_qtile_table(const int32_t* seg, int B, int N, int tq, int tk, bool causal,
                               int2* tab, hipStream_t s);

@@ -8,10 +8,13 @@ import numpy as np
 
 # Bounds (see the test docstrings): bf16 inputs: O max-abs <= max(1e-2, one bf16
 # ulp of the exact value), dQ/dK/dV relative L2 <= 2e-2; fp32 inputs: O max-abs
-# <= 1e-4 and relative L2 <= 1e-4.  LSE (internal check): 1e-3 / 1e-5.
+# <= 1e-4 and relative L2 <= 1e-4.  LSE (internal check): 1e-3 / 1e-5, relative
+# to |LSE| once that exceeds 10 (the kernels hold LSE in fp32, whose ulp alone
+# passes 1e-5 above 128).
 O_ABS = {"bf16": 1e-2, "fp32": 1e-4}
 REL_L2 = {"bf16": 2e-2, "fp32": 1e-4}
 LSE_ABS = {"bf16": 1e-3, "fp32": 1e-5}
+LSE_SCALE_FROM = 10.0
 
 
 def say(msg: str) -> None:
@@ -75,9 +78,12 @@ def check_grad(g: np.ndarray, r: np.ndarray, dtype: str, what: str) -> float:
 
 
 def check_lse(l_gpu: np.ndarray, l_ref: np.ndarray, dtype: str) -> float:
-    e = float(np.abs(l_gpu - l_ref).max())
-    assert e <= LSE_ABS[dtype], f"LSE max-abs {e:.3e} > {LSE_ABS[dtype]}"
-    return e
+    err = np.abs(l_gpu - l_ref)
+    bound = LSE_ABS[dtype] * np.maximum(1.0, np.abs(l_ref) / LSE_SCALE_FROM)
+    bad = err > bound
+    assert not bad.any(), (f"LSE: {int(bad.sum())} over bound, worst err {err.max():.3e} "
+                           f"at |LSE| {np.abs(l_ref).ravel()[err.argmax()]:.3g}")
+    return float(err.max())
 
 
 def run_gpu(t: dict, seg, dtype: str, scale: float, causal: bool):

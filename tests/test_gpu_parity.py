@@ -96,6 +96,39 @@ def test_segment_ids_need_not_start_at_zero():
     _compare(out, _oracle_full(t, seg, 0.125, True), "bf16")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_rising_and_falling_scores(D, dtype):
+    """Scores that climb steeply along the keys move every row's softmax
+    reference again on nearly every key tile (the rare rescale path); scores
+    that fall keep the first tile's reference and underflow later tiles.
+
+    The forward outputs are checked in both dtypes.  With softmax this sharp,
+    P is one-hot to bf16 precision and dS = P (dP - D_i) is dominated by the
+    cancellation of dP against D_i, which the method takes from the stored
+    (bf16-rounded) O; in bf16 that difference is rounding noise on both
+    sides, so dQ and dK are checked in fp32 only and dV (no D_i term) in
+    both."""
+    B, H, N = 1, 2, 300
+    say(f"rising/falling scores B1 H2 N300 D{D} {dtype}")
+    t = workloads.make_tensors(B, H, N, D, dtype, 79)
+    ramp = (np.arange(N) / N * 8.0)[:, None] * np.ones((1, D))
+    t["q"] = t["q"] * 0.25 + 2.0
+    t["k"] = t["k"] * 0.25 + np.stack([ramp, ramp[::-1]])[None]   # head 0 rises, head 1 falls
+    if dtype == "bf16":
+        t = {n: workloads.bf16_round(x) for n, x in t.items()}
+    scale = 1.0 / np.sqrt(D)
+    seg = workloads.random_segments(B, N, 79, max_len=120)
+    grads = ("dq", "dk", "dv") if dtype == "fp32" else ("dv",)
+    for sg in (None, seg):
+        out = run_gpu(t, sg, dtype, scale, True)
+        ref = _oracle_full(t, sg, scale, True)
+        check_o(down(out["o"]), ref["o"], dtype)
+        check_lse(down(out["lse"]), ref["lse"], dtype)
+        for n in grads:
+            check_grad(down(out[n]), ref[n], dtype, n)
+
+
 # ---------------------------------------------------------------- the workloads
 
 def test_tiny_fp32_one_segment():
