@@ -79,7 +79,8 @@ typedef enum fa_dtype {
  * this shape.  O(B*H*N): 256 bytes of flags, plus for the backward two fp32
  * (B, H, N) arrays (the row sums D_i = dO_i . O_i, stored negated, and the
  * log2-domain LSE), plus
- * with has_seg two per-tile range tables of B * ceil(N/32) int32 pairs.
+ * with has_seg two per-tile range tables of B * ceil(N/32) int32 pairs and
+ * two longest-first work lists of B * ceil(N/32) int32 quadruples.
  * Returns 0 for shapes fa_fwd / fa_bwd would refuse.
  */
 size_t fa_workspace_bytes(int B, int H, int N, int D, int has_seg, int for_bwd);

@@ -24,7 +24,7 @@ constexpr int kMinTile = 32;   // tables are sized for the smallest tile, so any
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-  size_t flag = 0, delta = 0, lse2 = 0, qtab = 0, ktab = 0, total = 0;
+  size_t flag = 0, delta = 0, lse2 = 0, qtab = 0, ktab = 0, qwork = 0, kwork = 0, total = 0;
 };
 
 bool shape_ok(int B, int H, int N) {
@@ -45,11 +45,16 @@ Layout layout(int B, int H, int N, bool has_seg, bool for_bwd) {
     off += vec;
   }
   if (has_seg) {
-    const size_t tab = align_up((size_t)B * ((N + kMinTile - 1) / kMinTile) * sizeof(int2));
+    const size_t tiles = (size_t)B * ((N + kMinTile - 1) / kMinTile);
+    const size_t tab = align_up(tiles * sizeof(int2)), work = align_up(tiles * sizeof(int4));
     L.qtab = off;
     off += tab;
     L.ktab = off;
     off += tab;
+    L.qwork = off;
+    off += work;
+    L.kwork = off;
+    off += work;
   }
   L.total = off;
   return L;
@@ -130,7 +135,7 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   p.o = o;
   p.lse = lse;
   p.seg = seg;
-  p.qtab = seg ? (const int2*)(w + L.qtab) : nullptr;
+  p.work = seg ? (const int4*)(w + L.qwork) : nullptr;
   p.B = B;
   p.H = H;
   p.N = N;
@@ -140,9 +145,10 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   p.scale = scale;
   p.c = log2e_scale(scale);
   if (seg) {
-    if (fa::launch_seg_check(seg, B, N, (int32_t*)(w + L.flag), s) != hipSuccess) return FA_ERR_HIP;
     if (fa::launch_qtile_table(seg, B, N, bm, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
-        hipSuccess)
+            hipSuccess ||
+        fa::launch_tile_order((const int2*)(w + L.qtab), B, p.nqt, (int4*)(w + L.qwork), seg, N,
+                              (int32_t*)(w + L.flag), s) != hipSuccess)
       return FA_ERR_HIP;
   }
   if (fa::launch_fwd(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
@@ -179,13 +185,16 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
 
   const int nw = fa::waves_for(seg != nullptr);
   const int bt = nw * 32;   // queries (dQ) or keys (dK/dV) per workgroup
+  const int ntiles = (N + bt - 1) / bt;
   if (seg) {
-    if (fa::launch_seg_check(seg, B, N, (int32_t*)(w + L.flag), s) != hipSuccess) return FA_ERR_HIP;
     if (fa::launch_qtile_table(seg, B, N, bt, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
-        hipSuccess)
-      return FA_ERR_HIP;
-    if (fa::launch_ktile_table(seg, B, N, bt, fa::QRY_TILE, causal != 0, (int2*)(w + L.ktab), s) !=
-        hipSuccess)
+            hipSuccess ||
+        fa::launch_ktile_table(seg, B, N, bt, fa::QRY_TILE, causal != 0, (int2*)(w + L.ktab), s) !=
+            hipSuccess ||
+        fa::launch_tile_order((const int2*)(w + L.qtab), B, ntiles, (int4*)(w + L.qwork), seg, N,
+                              (int32_t*)(w + L.flag), s) != hipSuccess ||
+        fa::launch_tile_order((const int2*)(w + L.ktab), B, ntiles, (int4*)(w + L.kwork), nullptr, N,
+                              nullptr, s) != hipSuccess)
       return FA_ERR_HIP;
   }
 
@@ -217,13 +226,13 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   p.c = log2e_scale(scale);
 
   if (!record(events, 1, s)) return FA_ERR_HIP;
-  p.tab = seg ? (const int2*)(w + L.ktab) : nullptr;
-  p.ntiles = (N + bt - 1) / bt;
+  p.work = seg ? (const int4*)(w + L.kwork) : nullptr;
+  p.ntiles = ntiles;
   if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
 
   if (!record(events, 2, s)) return FA_ERR_HIP;
-  p.tab = seg ? (const int2*)(w + L.qtab) : nullptr;
-  p.ntiles = (N + bt - 1) / bt;
+  p.work = seg ? (const int4*)(w + L.qwork) : nullptr;
+  p.ntiles = ntiles;
   if (fa::launch_bwd_dq(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
   if (!record(events, 3, s)) return FA_ERR_HIP;
   return FA_OK;

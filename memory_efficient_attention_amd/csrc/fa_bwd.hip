@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
   using StV = Stager<T, BN, D, NW, false>;
   constexpr int TK = LK::bytes(BN), TV = LV::bytes(BN);
   constexpr int S = sizeof(T) == 2 ? stages_for(FA_DQ_STAGES, TK + TV + BN * 4, NW) : 2;
-  static_assert(S >= 2, "two K/V stages must fit in LDS");
+  static_assert(S >= 2 && S * (TK + TV + BN * 4) <= LDS_PER_CU, "K/V stages must fit in LDS");
   constexpr int LPT = (StK::NINST + StV::NINST) / NW;
   // layout: K[S] | V[S] | seg[S]
   __shared__ __attribute__((aligned(1024))) char smem_raw[S * (TK + TV + BN * 4)];
@@ -80,33 +80,35 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
   const int N = p.N;
   const int nqt = p.ntiles;
 
-  const int total = p.B * p.H * nqt;
-  const int Lw = xcd_remap(blockIdx.x, total);
-  const int bh = Lw / nqt;
-  const int qt = nqt - 1 - (Lw - bh * nqt);
-  const int b = bh / p.H;
+  // (batch, head, query tile) and key-tile range, as in the forward.
+  const bool packed = p.seg != nullptr;
+  int bh, b, qt, kt_lo = 0, kt_hi;
+  if (packed) {
+    const int4 wk = p.work[blockIdx.x / p.H];
+    b = wk.x;
+    qt = wk.y;
+    kt_lo = wk.z;
+    kt_hi = wk.w;
+    bh = b * p.H + (int)(blockIdx.x % p.H);
+  } else {
+    const int Lw = xcd_remap(blockIdx.x, p.B * p.H * nqt);
+    bh = Lw / nqt;
+    qt = nqt - 1 - (Lw - bh * nqt);
+    b = bh / p.H;
+    kt_hi = ((CAUSAL ? min(qt * BM + BM, N) : N) - 1) / BN;
+  }
   const size_t off = (size_t)bh * N * D;
   const T* gq = (const T*)p.q + off;
   const T* gk = (const T*)p.k + off;
   const T* gv = (const T*)p.v + off;
   const T* gdo = (const T*)p.dO + off;
-  const int32_t* seg = p.seg ? p.seg + (size_t)b * N : nullptr;
-  const bool packed = seg != nullptr;
+  const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
 
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + col;
   const int qc = min(qi, N - 1);
   const int qlast = min(qw0 + 31, N - 1);
-
-  int kt_lo = 0, kt_hi;
-  if (packed) {
-    const int2 r = p.tab[(size_t)b * nqt + qt];
-    kt_lo = r.x;
-    kt_hi = r.y;
-  } else {
-    kt_hi = ((CAUSAL ? min(q0 + BM, N) : N) - 1) / BN;
-  }
 
   frag_t<T> qf[KS], dof[KS];
 #pragma unroll
@@ -246,7 +248,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   constexpr int TILE = L::bytes(BMQ);
   constexpr int VEC = BMQ * 4;
   constexpr int S = sizeof(T) == 2 ? stages_for(FA_DKV_STAGES, 2 * TILE + 3 * VEC, NW) : 2;
-  static_assert(S >= 2, "two Q/dO stages must fit in LDS");
+  static_assert(S >= 2 && S * (2 * TILE + 3 * VEC) <= LDS_PER_CU, "Q/dO stages must fit in LDS");
   constexpr int LPT = 2 * St::NINST / NW;
   __shared__ __attribute__((aligned(1024))) char smem_raw[S * (2 * TILE + 3 * VEC)];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
@@ -258,11 +260,26 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   const int N = p.N;
   const int nkt = p.ntiles;
 
-  const int total = p.B * p.H * nkt;
-  const int Lw = xcd_remap(blockIdx.x, total);
-  const int bh = Lw / nkt;
-  const int kt = Lw - bh * nkt;       // causal: key tile 0 sees the most queries
-  const int b = bh / p.H;
+  // (batch, head, key tile) and query-tile range.  Packed: the longest-first
+  // work list.  Dense: XCD-contiguous heads, key tile 0 (for causal, seen by
+  // the most queries) first.
+  const bool packed = p.seg != nullptr;
+  int bh, b, kt, qt_lo, qt_hi;
+  if (packed) {
+    const int4 wk = p.work[blockIdx.x / p.H];
+    b = wk.x;
+    kt = wk.y;
+    qt_lo = wk.z;
+    qt_hi = wk.w;
+    bh = b * p.H + (int)(blockIdx.x % p.H);
+  } else {
+    const int Lw = xcd_remap(blockIdx.x, p.B * p.H * nkt);
+    bh = Lw / nkt;
+    kt = Lw - bh * nkt;
+    b = bh / p.H;
+    qt_lo = CAUSAL ? kt * BNK / BMQ : 0;
+    qt_hi = (N - 1) / BMQ;
+  }
   const size_t off = (size_t)bh * N * D;
   const T* gq = (const T*)p.q + off;
   const T* gk = (const T*)p.k + off;
@@ -270,24 +287,13 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   const T* gdo = (const T*)p.dO + off;
   const float* glse2 = p.lse2 + (size_t)bh * N;
   const float* gdelta = p.delta + (size_t)bh * N;
-  const int32_t* seg = p.seg ? p.seg + (size_t)b * N : nullptr;
-  const bool packed = seg != nullptr;
+  const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
 
   const int k0 = kt * BNK;
   const int kw0 = k0 + wave * 32;
   const int kj = kw0 + col;
   const int kc_ = min(kj, N - 1);
   const int klast = min(kw0 + 31, N - 1);
-
-  int qt_lo, qt_hi;
-  if (packed) {
-    const int2 r = p.tab[(size_t)b * nkt + kt];
-    qt_lo = r.x;
-    qt_hi = r.y;
-  } else {
-    qt_lo = CAUSAL ? k0 / BMQ : 0;
-    qt_hi = (N - 1) / BMQ;
-  }
 
   frag_t<T> kf[KS], vf[KS];
 #pragma unroll

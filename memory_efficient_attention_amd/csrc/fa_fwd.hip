@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
   using StV = Stager<T, BN, D, NW, true>;
   constexpr int TK = LK::bytes(BN), TV = LV::bytes(BN);
   constexpr int S = sizeof(T) == 2 ? stages_for(FA_FWD_STAGES, TK + TV + BN * 4, NW) : 2;
-  static_assert(S >= 2, "two K/V stages must fit in LDS");
+  static_assert(S >= 2 && S * (TK + TV + BN * 4) <= LDS_PER_CU, "K/V stages must fit in LDS");
   constexpr int LPT = (StK::NINST + StV::NINST) / NW;   // loads per wave per tile, at least
   // layout: K[S] | V[S] | seg[S]
   __shared__ __attribute__((aligned(1024))) char smem_raw[S * (TK + TV + BN * 4)];
@@ -46,17 +46,30 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
   const int h = lane >> 5, col = lane & 31;
   const int N = p.N;
 
-  const int total = p.B * p.H * p.nqt;
-  const int Lw = xcd_remap(blockIdx.x, total);
-  const int bh = Lw / p.nqt;
-  const int qt = p.nqt - 1 - (Lw - bh * p.nqt);   // longest query tiles first
-  const int b = bh / p.H;
+  // Which (batch, head, query tile), and the key tiles to walk.  Packed: the
+  // longest-first work list.  Dense: each XCD takes a contiguous range of
+  // heads, the last (for causal, longest) query tiles first.
+  const bool packed = p.seg != nullptr;
+  int bh, b, qt, kt_lo = 0, kt_hi;
+  if (packed) {
+    const int4 wk = p.work[blockIdx.x / p.H];
+    b = wk.x;
+    qt = wk.y;
+    kt_lo = wk.z;
+    kt_hi = wk.w;
+    bh = b * p.H + (int)(blockIdx.x % p.H);
+  } else {
+    const int Lw = xcd_remap(blockIdx.x, p.B * p.H * p.nqt);
+    bh = Lw / p.nqt;
+    qt = p.nqt - 1 - (Lw - bh * p.nqt);
+    b = bh / p.H;
+    kt_hi = ((CAUSAL ? min(qt * BM + BM, N) : N) - 1) / BN;
+  }
   const size_t off = (size_t)bh * N * D;
   const T* gq = (const T*)p.q + off;
   const T* gk = (const T*)p.k + off;
   const T* gv = (const T*)p.v + off;
-  const int32_t* seg = p.seg ? p.seg + (size_t)b * N : nullptr;
-  const bool packed = seg != nullptr;
+  const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
 
   // The wave owns queries qw0 .. qw0 + 31; lane l holds query qw0 + l % 32.
   const int q0 = qt * BM;
@@ -64,15 +77,6 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
   const int qi = qw0 + col;
   const int qc = min(qi, N - 1);
   const int qlast = min(qw0 + 31, N - 1);
-
-  int kt_lo = 0, kt_hi;
-  if (packed) {
-    const int2 r = p.qtab[(size_t)b * p.nqt + qt];
-    kt_lo = r.x;
-    kt_hi = r.y;
-  } else {
-    kt_hi = ((CAUSAL ? min(q0 + BM, N) : N) - 1) / BN;
-  }
 
   frag_t<T> qf[KS];
 #pragma unroll

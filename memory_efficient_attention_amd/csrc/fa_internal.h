@@ -59,8 +59,10 @@ constexpr int waves_for(bool packed) { return packed ? WAVES_PACKED : WAVES_DENS
 // fits its share of the CU's LDS (WAVES_PER_CU / NW workgroups share a CU)
 // at `per_stage` bytes per stage (fp32 tiles are twice as large).
 constexpr int stages_for(int requested, int per_stage, int nw) {
-  const int fit = LDS_PER_CU / (WAVES_PER_CU / nw) / per_stage;
-  return requested < fit ? requested : fit;
+  const int share = LDS_PER_CU / (WAVES_PER_CU >= nw ? WAVES_PER_CU / nw : 1);
+  const int fit = share / per_stage;
+  // two stages at least, even if that leaves fewer workgroups per CU
+  return requested < fit ? requested : (fit > 2 ? fit : 2);
 }
 
 // Online softmax with a lazily moved reference: probabilities are taken
@@ -76,7 +78,9 @@ struct FwdParams {
   void* o;
   float* lse;
   const int32_t* seg;    // (B, N) or null
-  const int2* qtab;      // per query tile: [first, last] key tile (packed only)
+  // packed only: {b, query tile, first key tile, last key tile} per query
+  // tile, longest first; workgroup w runs head w % H of entry w / H
+  const int4* work;
   int B, H, N, nqt;
   float scale;           // softmax scale
   float c;               // scale * log2(e)
@@ -93,7 +97,10 @@ struct BwdParams {
   const float* lse2;     // log2-domain LSE (B, H, N)
   const float* delta;    // -D_i = -dO_i . O_i (B, H, N)
   const int32_t* seg;
-  const int2* tab;       // dQ: per query tile key-tile range; dK/dV: per key tile query-tile range
+  // packed only, longest first: dQ {b, query tile, first, last key tile};
+  // dK/dV {b, key tile, first, last query tile}; workgroup w runs head
+  // w % H of entry w / H
+  const int4* work;
   int B, H, N, ntiles;
   float scale, c;
 };
@@ -135,6 +142,9 @@ hipError_t launch_qtile_table(const int32_t* seg, int B, int N, int tq, int tk, 
                               int2* tab, hipStream_t s);
 hipError_t launch_ktile_table(const int32_t* seg, int B, int N, int tk, int tq, bool causal,
                               int2* tab, hipStream_t s);
-hipError_t launch_seg_check(const int32_t* seg, int B, int N, int32_t* flag, hipStream_t s);
+// Longest-first work list {b, tile, first, last} from a range table of B x nt
+// tiles (and, with check_seg, the segment-order check into flag).
+hipError_t launch_tile_order(const int2* tab, int B, int nt, int4* work, const int32_t* check_seg, int N,
+                             int32_t* flag, hipStream_t s);
 
 }  // namespace fa

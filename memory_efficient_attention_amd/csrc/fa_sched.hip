@@ -13,7 +13,9 @@
 //
 // start/end come from binary search on the row, valid because ids are
 // non-decreasing; rows that violate this get clamped, in-range tables (and
-// the check kernel raises the workspace flag).
+// the order kernel raises the workspace flag).  Workgroups then take the
+// tiles longest first, so the heaviest (long-segment) tiles do not start
+// last and stretch the launch.
 #include "fa_internal.h"
 
 namespace fa {
@@ -74,15 +76,47 @@ __global__ void __launch_bounds__(256) ktile_table_kernel(const int32_t* seg, in
   tab[t] = make_int2(lo / tq, hi / tq);
 }
 
-// flag[0] = 1 if some row's ids decrease, else 0.  One workgroup.
-__global__ void __launch_bounds__(1024) seg_check_kernel(const int32_t* seg, int B, int N, int32_t* flag) {
-  int bad = 0;
-  const long long n = (long long)B * N;
-  for (long long i = threadIdx.x; i < n; i += 1024) {
-    if ((i % N) != N - 1 && seg[i] > seg[i + 1]) bad = 1;
+// Longest-first work list from a range table of n = B * nt tiles: work[k] =
+// {b, tile, first, last} with k ordered by descending range length (clamped
+// to 255 tiles), by a counting sort in LDS.  Ties come out in any order; the
+// order only decides which workgroup starts first, never what a workgroup
+// computes.  With seg given, also flag[0] = 1 if some row's ids decrease,
+// else 0.  One workgroup.
+__global__ void __launch_bounds__(1024) order_kernel(const int2* tab, int n, int nt, int4* work,
+                                                     const int32_t* seg, int B, int N, int32_t* flag) {
+  constexpr int NB = 256;
+  __shared__ int cnt[NB];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < NB; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  auto bucket = [&](int i) {
+    const int2 r = tab[i];
+    return NB - 1 - clampi(r.y - r.x + 1, 0, NB - 1);   // longest first
+  };
+  for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[bucket(i)], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int k = 0; k < NB; ++k) {
+      const int c = cnt[k];
+      cnt[k] = acc;
+      acc += c;
+    }
   }
-  bad = __syncthreads_or(bad);
-  if (threadIdx.x == 0) flag[0] = bad ? 1 : 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) {
+    const int2 r = tab[i];
+    work[atomicAdd(&cnt[bucket(i)], 1)] = make_int4(i / nt, i % nt, r.x, r.y);
+  }
+  if (seg) {
+    int bad = 0;
+    const long long m = (long long)B * N;
+    for (long long i = tid; i < m; i += 1024) {
+      if ((i % N) != N - 1 && seg[i] > seg[i + 1]) bad = 1;
+    }
+    bad = __syncthreads_or(bad);
+    if (tid == 0) flag[0] = bad ? 1 : 0;
+  }
 }
 
 hipError_t launch_qtile_table(const int32_t* seg, int B, int N, int tq, int tk, bool causal,
@@ -101,8 +135,9 @@ hipError_t launch_ktile_table(const int32_t* seg, int B, int N, int tk, int tq, 
   return hipGetLastError();
 }
 
-hipError_t launch_seg_check(const int32_t* seg, int B, int N, int32_t* flag, hipStream_t s) {
-  hipLaunchKernelGGL(seg_check_kernel, dim3(1), dim3(1024), 0, s, seg, B, N, flag);
+hipError_t launch_tile_order(const int2* tab, int B, int nt, int4* work, const int32_t* check_seg, int N,
+                             int32_t* flag, hipStream_t s) {
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s, tab, B * nt, nt, work, check_seg, B, N, flag);
   return hipGetLastError();
 }
 

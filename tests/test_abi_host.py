@@ -120,8 +120,10 @@ def test_workspace_sizes(lib):
     # O(N): two fp32 (B,H,N) arrays plus a 256-byte flag block
     assert b1 == 256 + 2 * 32 * 8192 * 4 and b2 == 256 + 2 * 32 * 16384 * 4
     s1 = ws(4, 32, 4096, 128, 1, 1)
-    assert s1 == 256 + 2 * 4 * 32 * 4096 * 4 + 2 * 4 * (4096 // 32) * 8
-    assert ws(1, 1, 100, 64, 1, 0) == 256 + 2 * 256           # tables rounded to 256 B
+    # + two range tables (int32 pairs) and two work lists (int32 quadruples)
+    # per tile of 32
+    assert s1 == 256 + 2 * 4 * 32 * 4096 * 4 + 2 * 4 * (4096 // 32) * (8 + 16)
+    assert ws(1, 1, 100, 64, 1, 0) == 256 + 4 * 256           # each rounded to 256 B
     for n in (1000, 2000, 4000):
         assert ws(1, 8, 2 * n, 64, 1, 1) - 256 <= 2.01 * (ws(1, 8, n, 64, 1, 1) - 256)
 
