@@ -30,6 +30,13 @@ visibility mask over all N keys (no tile skipping, no online softmax):
   recomputes the tiles it needs from the saved state.  They follow from the
   chain rule through softmax: dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik).
 
+* Grouped-query heads.  K and V may carry Hkv heads for H query heads (H a
+  multiple of Hkv); query head h then reads key/value head h // (H / Hkv), the
+  groups being contiguous runs of query heads as the mlx-train-perf README
+  states for its attention op (section "If you maintain a trainer": grouped
+  query heads mapped contiguously).  dK and dV of a key/value head are sums
+  over the query heads that read it.
+
 All arithmetic is float64 on the exact values the GPU receives.  Rows are
 processed in blocks of ``row_block`` queries purely to bound memory; each block
 still builds the explicit mask over every key.
@@ -68,12 +75,22 @@ def _row_lse(s: np.ndarray) -> np.ndarray:
     return m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
 
 
+def _group(q, k):
+    """Query heads per key/value head."""
+    H, Hkv = q.shape[1], k.shape[1]
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"{H} query heads do not split into groups over {Hkv} key/value heads")
+    return H // Hkv
+
+
 def attention_forward(q, k, v, seg=None, scale=None, causal=True, row_block=512):
-    """O (B,H,N,D) and LSE (B,H,N), float64.  ``seg`` is (B,N) ints or None."""
+    """O (B,H,N,D) and LSE (B,H,N), float64.  ``seg`` is (B,N) ints or None;
+    k and v are (B,Hkv,N,D) with Hkv dividing H."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, N, D = q.shape
+    G = _group(q, k)
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     scale = float(scale)
@@ -85,17 +102,18 @@ def attention_forward(q, k, v, seg=None, scale=None, causal=True, row_block=512)
             rows = np.arange(r0, min(r0 + row_block, N))
             mask = visible_mask(rows, N, seg_row, causal)
             for h in range(H):
-                s = _scores(q[b, h, rows], k[b, h], scale, mask)
+                g = h // G
+                s = _scores(q[b, h, rows], k[b, g], scale, mask)
                 l = _row_lse(s)
                 p = np.exp(s - l[:, None])
-                o[b, h, rows] = p @ v[b, h]
+                o[b, h, rows] = p @ v[b, g]
                 lse[b, h, rows] = l
     return o, lse
 
 
 def attention_backward(q, k, v, do, seg=None, scale=None, causal=True,
                        o=None, lse=None, row_block=512):
-    """dQ, dK, dV (B,H,N,D) float64 for loss gradient ``do``.
+    """dQ (B,H,N,D), dK and dV (B,Hkv,N,D), float64, for loss gradient ``do``.
 
     O and LSE are the oracle's own fp64 forward results; they are recomputed
     when not passed in.
@@ -105,6 +123,7 @@ def attention_backward(q, k, v, do, seg=None, scale=None, causal=True,
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     B, H, N, D = q.shape
+    G = _group(q, k)
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     scale = float(scale)
@@ -119,14 +138,15 @@ def attention_backward(q, k, v, do, seg=None, scale=None, causal=True,
             rows = np.arange(r0, min(r0 + row_block, N))
             mask = visible_mask(rows, N, seg_row, causal)
             for h in range(H):
-                s = _scores(q[b, h, rows], k[b, h], scale, mask)
+                g = h // G
+                s = _scores(q[b, h, rows], k[b, g], scale, mask)
                 p = np.exp(s - lse[b, h, rows][:, None])
-                dp = do[b, h, rows] @ v[b, h].T
+                dp = do[b, h, rows] @ v[b, g].T
                 dr = np.sum(do[b, h, rows] * o[b, h, rows], axis=1)
                 ds = p * (dp - dr[:, None])
-                dq[b, h, rows] = scale * (ds @ k[b, h])
-                dk[b, h] += scale * (ds.T @ q[b, h, rows])
-                dv[b, h] += p.T @ do[b, h, rows]
+                dq[b, h, rows] = scale * (ds @ k[b, g])
+                dk[b, g] += scale * (ds.T @ q[b, h, rows])
+                dv[b, g] += p.T @ do[b, h, rows]
     return dq, dk, dv
 
 

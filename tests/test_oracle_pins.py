@@ -150,6 +150,38 @@ def test_finite_differences(N, D, causal, packed):
         assert err < 1e-6, err
 
 
+@pytest.mark.parametrize("Hkv,causal,packed", [(2, True, False), (1, True, True), (2, False, True)])
+def test_finite_differences_grouped_heads(Hkv, causal, packed):
+    """Grouped-query heads: 4 query heads over Hkv key/value heads."""
+    B, H, N, D = 1, 4, 5, 4
+    q, do = (_rand((B, H, N, D), 300 + s) for s in range(2))
+    k, v = (_rand((B, Hkv, N, D), 310 + s) for s in range(2))
+    seg = workloads.random_segments(B, N, 7, max_len=3) if packed else None
+    scale = 0.45
+    grads = attention_backward(q, k, v, do, seg, scale, causal)
+    assert grads[1].shape == k.shape and grads[2].shape == v.shape
+    h = 1e-6
+    for x, g in zip((q, k, v), grads):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss(q, k, v, do, seg, scale, causal)
+            x[idx] = old - h
+            lm = _loss(q, k, v, do, seg, scale, causal)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.abs(fd - g).max() / max(1.0, np.abs(g).max())
+        assert err < 1e-6, err
+
+
+def test_grouped_heads_refuse_uneven_groups():
+    q = np.zeros((1, 4, 3, 4))
+    k = np.zeros((1, 3, 3, 4))
+    with pytest.raises(ValueError):
+        attention_forward(q, k, k)
+
+
 # ---------------------------------------------------------------- invariants
 
 def test_packed_row_equals_segments_alone():
@@ -255,6 +287,24 @@ def test_visible_pairs_closed_form():
     assert visible_pairs(N, seg, causal=False) == sum(L * L for L in lens)
 
 
+def test_gradient_sums_per_segment_grouped_heads():
+    """With K/V shared by a group of query heads, dK of a key/value head still
+    sums to 0 over each segment, and dV sums to the group's summed dO."""
+    B, H, Hkv, N, D = 1, 6, 2, 40, 8
+    q, do = (_rand((B, H, N, D), 320 + s) for s in range(2))
+    k, v = (_rand((B, Hkv, N, D), 330 + s) for s in range(2))
+    seg = workloads.random_segments(B, N, 8, max_len=12)
+    dq, dk, dv = attention_backward(q, k, v, do, seg, 0.3, True)
+    grouped_do = do.reshape(B, Hkv, H // Hkv, N, D).sum(axis=2)
+    start = 0
+    for L in workloads.segment_lengths(seg[0]):
+        sl = slice(start, start + L)
+        assert np.abs(dk[0, :, sl].sum(axis=1)).max() < 1e-12
+        np.testing.assert_allclose(dv[0, :, sl].sum(axis=1), grouped_do[0, :, sl].sum(axis=1),
+                                   rtol=0, atol=1e-12)
+        start += L
+
+
 # ---------------------------------------------------------------- library cross-check
 
 def test_against_torch_sdpa_fp64():
@@ -285,3 +335,25 @@ def test_against_torch_sdpa_fp64():
             np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-11, atol=1e-11)
             np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-11)
             np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-11)
+
+
+def test_grouped_heads_against_torch_sdpa_fp64():
+    """torch's SDPA with enable_gqa repeats each key/value head over a
+    contiguous run of query heads, the convention the oracle follows."""
+    torch = pytest.importorskip("torch")
+    if "enable_gqa" not in (torch.nn.functional.scaled_dot_product_attention.__doc__ or ""):
+        pytest.skip("this torch has no grouped-query SDPA")
+    B, H, Hkv, N, D = 2, 6, 2, 20, 8
+    q, do = (_rand((B, H, N, D), 340 + s) for s in range(2))
+    k, v = (_rand((B, Hkv, N, D), 350 + s) for s in range(2))
+    scale = 0.3
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale,
+                                                           enable_gqa=True)
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    o, _ = attention_forward(q, k, v, None, scale, True)
+    dq, dk, dv = attention_backward(q, k, v, do, None, scale, True)
+    np.testing.assert_allclose(o, out.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-11)
