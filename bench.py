@@ -129,7 +129,7 @@ def run_workload(w, steps: int, warmup: int, seg_override="keep", causal=True, q
     B, H, N, D = w.B, w.H, w.N, w.D
     o = torch.empty_like(x["q"])
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
+    dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
     ws_f = torch.empty(max(fa.fa_workspace_bytes(B, H, N, D, seg is not None, False), 256),
                        dtype=torch.uint8, device=dev)
     ws_b = torch.empty(fa.fa_workspace_bytes(B, H, N, D, seg is not None, True), dtype=torch.uint8,
@@ -200,8 +200,9 @@ def cpu_baseline(w, t_np, seg_np, causal=True):
     seg_row = None if seg_np is None else seg_np[b]
     V, nrows, heads, el = 0, 0, set(), 0.0
     t0 = time.perf_counter()
+    G = w.H // w.Hkv
     for h in range(w.H):
-        s = {n: a[b, h] for n, a in t_np.items()}
+        s = {n: a[b, h // G if n in ("k", "v") else h] for n, a in t_np.items()}
         for hi in range(w.N, 0, -CPU_BLOCK_ROWS):
             rows = np.arange(max(0, hi - CPU_BLOCK_ROWS), hi)
             o_r, lse_r = attention_rows(s["q"], s["k"], s["v"], rows, seg_row, w.scale, causal)
@@ -265,7 +266,7 @@ def headline(args):
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) q, k, v, dO)",
         "config": {"workload": f"{w.name}: {w.note}", "global_batch": w.B, "seq_len": w.N,
-                   "heads": w.H, "head_dim": w.D, "causal": True,
+                   "heads": w.H, "kv_heads": w.Hkv, "head_dim": w.D, "causal": True,
                    "segments": "none" if w.layout == "none" else w.layout,
                    "visible_pairs": res["V"], "visible_flops": res["flops"]},
         "pct_bf16_peak": round(100.0 * res["tflops"] / PEAK_BF16_TFLOPS, 2),
@@ -282,7 +283,7 @@ def report_all(args):
     import workloads
     rows = []
     names = ["tiny_causal_fp32", "causal_2k", "packed_short_4k", "single_segment_8k", "causal_16k",
-             "packed_long_64k"]
+             "packed_long_64k", "gqa_8k"]
     for name in names:
         w = workloads.get(name)
         print(f"# running {name}", file=sys.stderr, flush=True)

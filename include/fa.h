@@ -17,6 +17,11 @@
  *     the element type `dtype` (bf16 or fp32), D in {64, 128}, as in the
  *     README's "If you maintain a trainer" section ((B, H, N, D) with head_dim
  *     in {64, 96, 128}; 96 is not built yet and is refused).
+ *   - Grouped-query heads (same section: grouped query heads mapped
+ *     contiguously): k, v, dk and dv have Hkv heads, H a multiple of Hkv, and
+ *     query head h reads key/value head h / (H / Hkv).  Hkv = H is plain
+ *     multi-head attention.  dk and dv of a key/value head are the sums over
+ *     its H / Hkv query heads, formed inside one workgroup (no atomics).
  *   - `lse` is a (B, H, N) fp32 device buffer holding the natural-log
  *     log-sum-exp of scale * q_i . k_j over the keys row i may see.
  *   - `seg` is NULL (no packing) or a (B, N) int32 device buffer of segment ids
@@ -53,7 +58,8 @@ extern "C" {
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = 1,       /* a required pointer is NULL */
-    FA_ERR_SHAPE = 2,      /* B, H or N < 1, or sizes beyond the supported range */
+    FA_ERR_SHAPE = 2,      /* B, H, Hkv or N < 1, H not a multiple of Hkv, or sizes
+                              beyond the supported range */
     FA_ERR_HEAD_DIM = 3,   /* D not in {64, 128} */
     FA_ERR_DTYPE = 4,      /* dtype is neither FA_BF16 nor FA_FP32 (fp16 is refused) */
     FA_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than fa_workspace_bytes() */
@@ -77,8 +83,8 @@ typedef enum fa_dtype {
 /*
  * Bytes of workspace fa_fwd (for_bwd = 0) or fa_bwd (for_bwd = 1) needs for
  * this shape.  O(B*H*N): 256 bytes of flags, plus for the backward two fp32
- * (B, H, N) arrays (the row sums D_i = dO_i . O_i, stored negated, and the
- * log2-domain LSE), plus
+ * (B, H, N) arrays (the row sums D_i = dO_i . O_i and LSE / scale, both
+ * stored negated), plus
  * with has_seg two per-tile range tables of B * ceil(N/32) int32 pairs and
  * two longest-first work lists of B * ceil(N/32) int32 quadruples.
  * Returns 0 for shapes fa_fwd / fa_bwd would refuse.
@@ -87,7 +93,8 @@ size_t fa_workspace_bytes(int B, int H, int N, int D, int has_seg, int for_bwd);
 
 /*
  * Forward pass.  Writes o = softmax(scale * q k^T, masked) v and lse.
- *   q, k, v : (B, H, N, D) `dtype`, read only.
+ *   q       : (B, H, N, D) `dtype`, read only.
+ *   k, v    : (B, Hkv, N, D) `dtype`, read only.
  *   seg     : (B, N) int32 or NULL.
  *   scale   : softmax scale (typically 1/sqrt(D)), finite and > 0.
  *   causal  : non-zero for causal masking.
@@ -98,7 +105,7 @@ size_t fa_workspace_bytes(int B, int H, int N, int D, int has_seg, int for_bwd);
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, const int32_t* seg,
                  float scale, int causal, void* o, float* lse,
-                 int B, int H, int N, int D, fa_dtype dtype,
+                 int B, int H, int Hkv, int N, int D, fa_dtype dtype,
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -106,17 +113,20 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, const int32_t* seg
  * Recomputes P = exp(scale q k^T - lse) tile by tile and writes
  *   dq = scale * dS k,  dk = scale * dS^T q,  dv = P^T dO,
  * with dS = P * (dO v^T - D_i) and D_i = dO_i . O_i taken from the stored o.
- *   q, k, v, o, dO : (B, H, N, D) `dtype`, read only; o and lse come from
+ *   q, o, dO       : (B, H, N, D) `dtype`, read only; o and lse come from
  *                    fa_fwd with the same q, k, v, seg, scale and causal.
+ *   k, v           : (B, Hkv, N, D) `dtype`, read only.
  *   lse            : (B, H, N) fp32 from fa_fwd.
  *   seg, scale, causal : must equal the forward's.
- *   dq, dk, dv     : (B, H, N, D) `dtype`, written.
+ *   dq             : (B, H, N, D) `dtype`, written.
+ *   dk, dv         : (B, Hkv, N, D) `dtype`, written (summed over each
+ *                    key/value head's query heads).
  *   ws             : workspace of at least fa_workspace_bytes(..., 1) bytes.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const void* dO, const float* lse, const int32_t* seg,
                  float scale, int causal, void* dq, void* dk, void* dv,
-                 int B, int H, int N, int D, fa_dtype dtype,
+                 int B, int H, int Hkv, int N, int D, fa_dtype dtype,
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -132,7 +142,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
 fa_status fa_bwd_timed(const void* q, const void* k, const void* v, const void* o,
                        const void* dO, const float* lse, const int32_t* seg,
                        float scale, int causal, void* dq, void* dk, void* dv,
-                       int B, int H, int N, int D, fa_dtype dtype,
+                       int B, int H, int Hkv, int N, int D, fa_dtype dtype,
                        void* ws, size_t ws_bytes, void* stream, void* const* events);
 
 /*

@@ -57,11 +57,12 @@ def load_library():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_workspace_bytes.restype = sz
-    lib.fa_fwd.argtypes = [vp, vp, vp, vp, f, i, vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, f, i, vp, vp, i, i, i, i, i, i, vp, sz, vp]
     lib.fa_fwd.restype = i
-    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
     lib.fa_bwd.restype = i
-    lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, vp, sz, vp, vp]
+    lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp,
+                                 vp]
     lib.fa_bwd_timed.restype = i
     lib.fa_check_seg.argtypes = [vp, i, i]
     lib.fa_check_seg.restype = i
@@ -123,12 +124,23 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def _kv_heads(q, k) -> int:
+    """Key/value heads of k (grouped-query attention when fewer than q's)."""
+    if k.dim() != 4:
+        raise ValueError("k must be (B, Hkv, N, D)")
+    return int(k.shape[1])
+
+
 def fa_fwd(q, k, v, seg=None, scale=None, causal=True, out=None, lse=None, workspace=None):
-    """Forward pass; returns (o, lse)."""
+    """Forward pass; returns (o, lse).  q is (B, H, N, D); k and v are
+    (B, Hkv, N, D) with Hkv dividing H (query head h reads key/value head
+    h // (H // Hkv))."""
     import torch
     B, H, N, D = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(name, t, (B, H, N, D), q.dtype)
+    Hkv = _kv_heads(q, k)
+    _check_tensor("q", q, (B, H, N, D), q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, Hkv, N, D), q.dtype)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -141,7 +153,7 @@ def fa_fwd(q, k, v, seg=None, scale=None, causal=True, out=None, lse=None, works
     if nbytes and (ws is None or ws.numel() < nbytes):
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_p, ctypes.c_float(scale),
-                    int(bool(causal)), o.data_ptr(), lse_t.data_ptr(), B, H, N, D,
+                    int(bool(causal)), o.data_ptr(), lse_t.data_ptr(), B, H, Hkv, N, D,
                     _dtype_code(q), ws.data_ptr() if (ws is not None and nbytes) else None,
                     nbytes, _stream())
     if st:
@@ -157,15 +169,19 @@ def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=N
     recorded between the backward kernels (fa_bwd_timed in the C ABI)."""
     import torch
     B, H, N, D = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+    Hkv = _kv_heads(q, k)
+    for name, t in (("q", q), ("o", o), ("do", do)):
         _check_tensor(name, t, (B, H, N, D), q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, Hkv, N, D), q.dtype)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_tensor(name, t, (B, H, N, D), q.dtype)
+    _check_tensor("dq", dq, (B, H, N, D), q.dtype)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, (B, Hkv, N, D), q.dtype)
     seg_p = _seg_ptr(seg, B, N)
     lib = load_library()
     nbytes = lib.fa_workspace_bytes(B, H, N, D, int(seg is not None), 1)
@@ -174,7 +190,7 @@ def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=N
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
             lse.data_ptr(), seg_p, ctypes.c_float(scale), int(bool(causal)),
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, _dtype_code(q),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, D, _dtype_code(q),
             ws.data_ptr(), nbytes, _stream())
     if events is None:
         st = lib.fa_bwd(*args)

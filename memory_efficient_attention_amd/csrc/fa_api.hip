@@ -24,7 +24,7 @@ constexpr int kMinTile = 32;   // tables are sized for the smallest tile, so any
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-  size_t flag = 0, delta = 0, lse2 = 0, qtab = 0, ktab = 0, qwork = 0, kwork = 0, total = 0;
+  size_t flag = 0, delta = 0, nls = 0, qtab = 0, ktab = 0, qwork = 0, kwork = 0, total = 0;
 };
 
 bool shape_ok(int B, int H, int N) {
@@ -41,7 +41,7 @@ Layout layout(int B, int H, int N, bool has_seg, bool for_bwd) {
     const size_t vec = align_up((size_t)B * H * N * sizeof(float));
     L.delta = off;
     off += vec;
-    L.lse2 = off;
+    L.nls = off;
     off += vec;
   }
   if (has_seg) {
@@ -90,8 +90,8 @@ fa_status device_ok() {
   return ok ? FA_OK : FA_ERR_DEVICE;
 }
 
-fa_status common_checks(int B, int H, int N, int D, fa_dtype dtype, float scale) {
-  if (!shape_ok(B, H, N)) return FA_ERR_SHAPE;
+fa_status common_checks(int B, int H, int Hkv, int N, int D, fa_dtype dtype, float scale) {
+  if (!shape_ok(B, H, N) || Hkv < 1 || H % Hkv != 0) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_DTYPE;
   // one head's (N, D) matrix is addressed with 32-bit byte offsets
@@ -110,10 +110,10 @@ FA_API size_t fa_workspace_bytes(int B, int H, int N, int D, int has_seg, int fo
 }
 
 FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32_t* seg, float scale,
-                        int causal, void* o, float* lse, int B, int H, int N, int D, fa_dtype dtype,
-                        void* ws, size_t ws_bytes, void* stream) {
+                        int causal, void* o, float* lse, int B, int H, int Hkv, int N, int D,
+                        fa_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (fa_status st = common_checks(B, H, N, D, dtype, scale)) return st;
+  if (fa_status st = common_checks(B, H, Hkv, N, D, dtype, scale)) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
       !aligned(seg, 4))
     return FA_ERR_ALIGN;
@@ -138,6 +138,7 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   p.work = seg ? (const int4*)(w + L.qwork) : nullptr;
   p.B = B;
   p.H = H;
+  p.G = H / Hkv;
   p.N = N;
   const int nw = fa::waves_for(seg != nullptr);
   const int bm = nw * 32;   // queries per workgroup
@@ -164,10 +165,10 @@ bool record(void* const* events, int i, hipStream_t s) {
 
 fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
                    const float* lse, const int32_t* seg, float scale, int causal, void* dq, void* dk,
-                   void* dv, int B, int H, int N, int D, fa_dtype dtype, void* ws, size_t ws_bytes,
-                   void* stream, void* const* events) {
+                   void* dv, int B, int H, int Hkv, int N, int D, fa_dtype dtype, void* ws,
+                   size_t ws_bytes, void* stream, void* const* events) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
-  if (fa_status st = common_checks(B, H, N, D, dtype, scale)) return st;
+  if (fa_status st = common_checks(B, H, Hkv, N, D, dtype, scale)) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(seg, 4))
     return FA_ERR_ALIGN;
@@ -181,19 +182,23 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   char* w = (char*)ws;
   const int dt = dtype == FA_BF16 ? 0 : 1;
   float* delta = (float*)(w + L.delta);
-  float* lse2 = (float*)(w + L.lse2);
+  float* nls = (float*)(w + L.nls);
 
+  // dQ: waves per workgroup by masking; dK/dV: grouped heads divide its
+  // workgroups by H / Hkv, so it uses the smaller workgroups there too.
   const int nw = fa::waves_for(seg != nullptr);
-  const int bt = nw * 32;   // queries (dQ) or keys (dK/dV) per workgroup
+  const int nw_kv = fa::waves_for(seg != nullptr || Hkv != H);
+  const int bt = nw * 32;   // queries per dQ workgroup
   const int ntiles = (N + bt - 1) / bt;
+  const int ntiles_kv = (N + nw_kv * 32 - 1) / (nw_kv * 32);
   if (seg) {
     if (fa::launch_qtile_table(seg, B, N, bt, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
             hipSuccess ||
-        fa::launch_ktile_table(seg, B, N, bt, fa::QRY_TILE, causal != 0, (int2*)(w + L.ktab), s) !=
+        fa::launch_ktile_table(seg, B, N, nw_kv * 32, fa::QRY_TILE, causal != 0, (int2*)(w + L.ktab), s) !=
             hipSuccess ||
         fa::launch_tile_order((const int2*)(w + L.qtab), B, ntiles, (int4*)(w + L.qwork), seg, N,
                               (int32_t*)(w + L.flag), s) != hipSuccess ||
-        fa::launch_tile_order((const int2*)(w + L.ktab), B, ntiles, (int4*)(w + L.kwork), nullptr, N,
+        fa::launch_tile_order((const int2*)(w + L.ktab), B, ntiles_kv, (int4*)(w + L.kwork), nullptr, N,
                               nullptr, s) != hipSuccess)
       return FA_ERR_HIP;
   }
@@ -204,7 +209,8 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   pp.dO = dO;
   pp.lse = lse;
   pp.delta = delta;
-  pp.lse2 = lse2;
+  pp.nls = nls;
+  pp.scale = scale;
   pp.rows = (long long)B * H * N;
   if (fa::launch_bwd_pre(pp, dt, D, s) != hipSuccess) return FA_ERR_HIP;
 
@@ -216,19 +222,20 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.lse2 = lse2;
+  p.nls = nls;
   p.delta = delta;
   p.seg = seg;
   p.B = B;
   p.H = H;
+  p.G = H / Hkv;
   p.N = N;
   p.scale = scale;
   p.c = log2e_scale(scale);
 
   if (!record(events, 1, s)) return FA_ERR_HIP;
   p.work = seg ? (const int4*)(w + L.kwork) : nullptr;
-  p.ntiles = ntiles;
-  if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
+  p.ntiles = ntiles_kv;
+  if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, nw_kv, s) != hipSuccess) return FA_ERR_HIP;
 
   if (!record(events, 2, s)) return FA_ERR_HIP;
   p.work = seg ? (const int4*)(w + L.qwork) : nullptr;
@@ -242,17 +249,17 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
 
 FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                         const float* lse, const int32_t* seg, float scale, int causal, void* dq, void* dk,
-                        void* dv, int B, int H, int N, int D, fa_dtype dtype, void* ws, size_t ws_bytes,
-                        void* stream) {
-  return bwd_impl(q, k, v, o, dO, lse, seg, scale, causal, dq, dk, dv, B, H, N, D, dtype, ws, ws_bytes,
+                        void* dv, int B, int H, int Hkv, int N, int D, fa_dtype dtype, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dO, lse, seg, scale, causal, dq, dk, dv, B, H, Hkv, N, D, dtype, ws, ws_bytes,
                   stream, nullptr);
 }
 
 FA_API fa_status fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
                               const float* lse, const int32_t* seg, float scale, int causal, void* dq,
-                              void* dk, void* dv, int B, int H, int N, int D, fa_dtype dtype, void* ws,
-                              size_t ws_bytes, void* stream, void* const* events) {
-  return bwd_impl(q, k, v, o, dO, lse, seg, scale, causal, dq, dk, dv, B, H, N, D, dtype, ws, ws_bytes,
+                              void* dk, void* dv, int B, int H, int Hkv, int N, int D, fa_dtype dtype,
+                              void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  return bwd_impl(q, k, v, o, dO, lse, seg, scale, causal, dq, dk, dv, B, H, Hkv, N, D, dtype, ws, ws_bytes,
                   stream, events);
 }
 

@@ -19,8 +19,10 @@
 namespace fa {
 
 // ---------------------------------------------------------------- preprocess
-// delta[r] = -sum_d dO[r, d] * O[r, d] (O as stored; kept negated so the
-// consumers add it, or start an accumulator from it), lse2[r] = lse[r] * log2(e).
+// delta[r] = -sum_d dO[r, d] * O[r, d] (O as stored) and nls[r] = -lse[r] /
+// scale: both negated so that the dK/dV kernel can start its dP and S
+// accumulators from them (dP - D_i and S - LSE / scale come straight out of
+// the MFMAs) and the dQ kernel adds them.
 // LPR lanes share one row, each reading 16 contiguous bytes of O and dO.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
@@ -48,7 +50,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
   for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
   if (row < p.rows && sub == 0) {
     p.delta[row] = -acc;
-    p.lse2[row] = p.lse[row] * kLog2e;
+    p.nls[row] = -p.lse[row] / p.scale;
   }
 }
 
@@ -98,9 +100,10 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
     kt_hi = ((CAUSAL ? min(qt * BM + BM, N) : N) - 1) / BN;
   }
   const size_t off = (size_t)bh * N * D;
+  const size_t offkv = (size_t)(bh / p.G) * N * D;   // its key/value head
   const T* gq = (const T*)p.q + off;
-  const T* gk = (const T*)p.k + off;
-  const T* gv = (const T*)p.v + off;
+  const T* gk = (const T*)p.k + offkv;
+  const T* gv = (const T*)p.v + offkv;
   const T* gdo = (const T*)p.dO + off;
   const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
 
@@ -116,7 +119,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
     qf[ks] = gfrag_row<T, D>(gq, qc, 2 * ks + h);
     dof[ks] = gfrag_row<T, D>(gdo, qc, 2 * ks + h);
   }
-  const float lse2 = p.lse2[(size_t)bh * N + qc];
+  const float nlse2 = p.c * p.nls[(size_t)bh * N + qc];   // -LSE log2(e)
   const float ndlt = p.delta[(size_t)bh * N + qc];   // -D_i
   int segq = 0, segq_first = 0, segq_last = 0;
   if (packed) {
@@ -153,7 +156,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
     settle(qf[ks]);
     settle(dof[ks]);
   }
-  settle(lse2);
+  settle(nlse2);
   settle(ndlt);
   settle(segq);
   settle(segq_first);
@@ -209,7 +212,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
             const bool vis = key < N && (!CAUSAL || key <= qi) && (!packed || sk[i] == segq);
             if (!vis) s = -INFINITY;
           }
-          const float pv = exp2_fast(fmaf(s, c, -lse2));
+          const float pv = exp2_fast(fmaf(s, c, nlse2));
           sacc[kb][4 * j + i] = pv * (dpacc[kb][4 * j + i] + ndlt);
         }
       }
@@ -249,10 +252,15 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   constexpr int VEC = BMQ * 4;
   constexpr int S = sizeof(T) == 2 ? stages_for(FA_DKV_STAGES, 2 * TILE + 3 * VEC, NW) : 2;
   static_assert(S >= 2 && S * (2 * TILE + 3 * VEC) <= LDS_PER_CU, "Q/dO stages must fit in LDS");
-  constexpr int LPT = 2 * St::NINST / NW;
+  // Q and dO tiles share one stager's per-lane offsets when one tile's
+  // instructions already reach every wave; otherwise (D = 64, 8 waves) the
+  // dO stager continues the round-robin so that every wave has a load to
+  // count.
+  constexpr bool SHARE = St::NINST >= NW;
+  constexpr int LPT = SHARE ? 2 * (St::NINST / NW) : 2 * St::NINST / NW;
   __shared__ __attribute__((aligned(1024))) char smem_raw[S * (2 * TILE + 3 * VEC)];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
-  // layout: Q[S] | dO[S] | lse2[S] | delta[S] | seg[S]
+  // layout: Q[S] | dO[S] | nls[S] | delta[S] | seg[S]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -260,34 +268,43 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   const int N = p.N;
   const int nkt = p.ntiles;
 
-  // (batch, head, key tile) and query-tile range.  Packed: the longest-first
-  // work list.  Dense: XCD-contiguous heads, key tile 0 (for causal, seen by
-  // the most queries) first.
+  // (batch, key/value head, key tile) and query-tile range.  Packed: the
+  // longest-first work list.  Dense: XCD-contiguous heads, key tile 0 (for
+  // causal, seen by the most queries) first.  The workgroup walks the query
+  // tiles of each of the key/value head's G query heads in turn and sums
+  // their contributions to dK and dV in its registers.
   const bool packed = p.seg != nullptr;
-  int bh, b, kt, qt_lo, qt_hi;
+  const int G = p.G, Hkv = p.H / G;
+  int bg, b, kt, qt_lo, qt_hi;
   if (packed) {
-    const int4 wk = p.work[blockIdx.x / p.H];
+    const int4 wk = p.work[blockIdx.x / Hkv];
     b = wk.x;
     kt = wk.y;
     qt_lo = wk.z;
     qt_hi = wk.w;
-    bh = b * p.H + (int)(blockIdx.x % p.H);
+    bg = b * Hkv + (int)(blockIdx.x % Hkv);
   } else {
-    const int Lw = xcd_remap(blockIdx.x, p.B * p.H * nkt);
-    bh = Lw / nkt;
-    kt = Lw - bh * nkt;
-    b = bh / p.H;
+    const int Lw = xcd_remap(blockIdx.x, p.B * Hkv * nkt);
+    bg = Lw / nkt;
+    const int l = Lw - bg * nkt;
+    // With grouped heads there are few, long workgroups, all resident at
+    // once, so a head's first key tiles (heaviest under causal masking) are
+    // dispatched in ascending and its second half in descending order: the
+    // two workgroups a CU receives pair a heavy tile with a light one.
+    const int half = (nkt + 1) / 2;
+    kt = (G > 1 && l >= half) ? nkt - 1 - (l - half) : l;
+    b = bg / Hkv;
     qt_lo = CAUSAL ? kt * BNK / BMQ : 0;
     qt_hi = (N - 1) / BMQ;
   }
-  const size_t off = (size_t)bh * N * D;
-  const T* gq = (const T*)p.q + off;
-  const T* gk = (const T*)p.k + off;
-  const T* gv = (const T*)p.v + off;
-  const T* gdo = (const T*)p.dO + off;
-  const float* glse2 = p.lse2 + (size_t)bh * N;
-  const float* gdelta = p.delta + (size_t)bh * N;
+  const size_t offkv = (size_t)bg * N * D;
+  const size_t bh0 = (size_t)bg * G;   // first query head of the group
+  const T* gk = (const T*)p.k + offkv;
+  const T* gv = (const T*)p.v + offkv;
   const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
+  // iteration it covers query head bh0 + it / nq, query tile qt_lo + it % nq
+  const int nq = qt_hi - qt_lo + 1;
+  const int nit = nq > 0 ? G * nq : 0;
 
   const int k0 = kt * BNK;
   const int kw0 = k0 + wave * 32;
@@ -311,7 +328,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
 
   St stq, stdo;
   stq.init(wave, lane);
-  stdo.init(wave, lane, St::NINST);
+  if constexpr (!SHARE) stdo.init(wave, lane, St::NINST);
   const int rbase = L::row_base(lane);
   const int cbase = L::col_base(lane);
 
@@ -322,19 +339,21 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     dvacc[db] = f32x16{};
   }
 
-  auto stage = [&](int qt, int buf) {
-    const int r0 = qt * BMQ;
-    stq.issue(smem + buf * TILE, gq, r0, N);
-    stdo.issue(smem + (S + buf) * TILE, gdo, r0, N);
-    stage_vec<BMQ>(smem + 2 * S * TILE + buf * VEC, glse2, r0, N, wave, 0, lane);
-    stage_vec<BMQ>(smem + 2 * S * TILE + (S + buf) * VEC, gdelta, r0, N, wave, 1 % NW, lane);
+  auto stage = [&](int it, int buf) {
+    const int hj = it / nq;
+    const int r0 = (qt_lo + it - hj * nq) * BMQ;
+    const size_t bh = bh0 + hj;
+    stq.issue(smem + buf * TILE, (const T*)p.q + bh * N * D, r0, N);
+    (SHARE ? stq : stdo).issue(smem + (S + buf) * TILE, (const T*)p.dO + bh * N * D, r0, N);
+    stage_vec<BMQ>(smem + 2 * S * TILE + buf * VEC, p.nls + bh * N, r0, N, wave, 0, lane);
+    stage_vec<BMQ>(smem + 2 * S * TILE + (S + buf) * VEC, p.delta + bh * N, r0, N, wave, 1 % NW, lane);
     if (packed) stage_vec<BMQ>(smem + 2 * S * TILE + (2 * S + buf) * VEC, seg, r0, N, wave, 2 % NW, lane);
   };
 
   // Ring of S stages, as in the forward.
 #pragma unroll
   for (int i = 0; i < S - 1; ++i)
-    if (qt_lo + i <= qt_hi) stage(qt_lo + i, i);
+    if (i < nit) stage(i, i);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     settle(kf[ks]);
@@ -343,15 +362,16 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   settle(segk);
   settle(segk_first);
   settle(segk_last);
-  for (int qt = qt_lo; qt <= qt_hi; ++qt) {
-    const int buf = (qt - qt_lo) % S;
-    wait_tiles<LPT, S - 2>(qt_hi - qt);
+  for (int it = 0; it < nit; ++it) {
+    const int buf = it % S;
+    wait_tiles<LPT, S - 2>(nit - 1 - it);
     __syncthreads();
-    if (qt + S - 1 <= qt_hi) stage(qt + S - 1, buf == 0 ? S - 1 : buf - 1);
+    if (it + S - 1 < nit) stage(it + S - 1, buf == 0 ? S - 1 : buf - 1);
+    const int qt = qt_lo + it % nq;
 
     const FA_LDS char* Qs = smem + buf * TILE;
     const FA_LDS char* dOs = smem + (S + buf) * TILE;
-    const FA_LDS float* l2s = (const FA_LDS float*)(smem + 2 * S * TILE + buf * VEC);
+    const FA_LDS float* nls = (const FA_LDS float*)(smem + 2 * S * TILE + buf * VEC);
     const FA_LDS float* dls = (const FA_LDS float*)(smem + 2 * S * TILE + (S + buf) * VEC);
     const FA_LDS int* sqs = (const FA_LDS int*)(smem + 2 * S * TILE + (2 * S + buf) * VEC);
     const int q0 = qt * BMQ;
@@ -367,18 +387,21 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     }
     if (skip) continue;
 
-    // S = Q K^T and dP - D = dO V^T - D, block by block: the dP accumulator
-    // starts from -D_i (stored negated by the preprocess), so the MFMAs
-    // deliver dP - D directly.
+    // S - LSE / scale = Q K^T - LSE / scale and dP - D = dO V^T - D, block by
+    // block: the accumulators start from the preprocess's negated per-row
+    // values, so the MFMAs deliver both differences directly.
     f32x16 sacc[QB], dpacc[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      sacc[qb] = f32x16{};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const f32x4 nl = *(const FA_LDS f32x4*)(nls + 32 * qb + 8 * j + 4 * h);
         const f32x4 nd = *(const FA_LDS f32x4*)(dls + 32 * qb + 8 * j + 4 * h);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dpacc[qb][4 * j + i] = nd[i];
+        for (int i = 0; i < 4; ++i) {
+          sacc[qb][4 * j + i] = nl[i];
+          dpacc[qb][4 * j + i] = nd[i];
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -405,19 +428,15 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
       }
     }
 
-    // Per block: P = exp2(S c - lse2), dS = P (dP - D); then dV^T += dO^T P
-    // and dK^T += Q^T dS.
+    // Per block: P = exp2(c (S - LSE / scale)), dS = P (dP - D); then
+    // dV^T += dO^T P and dK^T += Q^T dS.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 l2 = *(const FA_LDS f32x4*)(l2s + 32 * qb + 8 * j + 4 * h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = exp2_fast(fmaf(sacc[qb][4 * j + i], c, -l2[i]));
-          sacc[qb][4 * j + i] = pv;
-          dpacc[qb][4 * j + i] = pv * dpacc[qb][4 * j + i];
-        }
+      for (int r = 0; r < 16; ++r) {
+        const float pv = exp2_fast(sacc[qb][r] * c);
+        sacc[qb][r] = pv;
+        dpacc[qb][r] = pv * dpacc[qb][r];
       }
       frag_t<T> pf[2], dsf[2];
 #pragma unroll
@@ -436,8 +455,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   }
 
   if (kj < N) {
-    store_rows<T, D>((T*)p.dk + off, kj, dkacc, p.scale, lane);
-    store_rows<T, D>((T*)p.dv + off, kj, dvacc, 1.f, lane);
+    store_rows<T, D>((T*)p.dk + offkv, kj, dkacc, p.scale, lane);
+    store_rows<T, D>((T*)p.dv + offkv, kj, dvacc, 1.f, lane);
   }
 }
 
@@ -472,7 +491,7 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, in
     using T = typename decltype(t)::type;
     constexpr int DD = decltype(d)::value, NW = decltype(w)::value;
     constexpr bool C = decltype(c)::value;
-    const long long total = (long long)p.B * p.H * p.ntiles;
+    const long long total = (long long)p.B * (p.H / p.G) * p.ntiles;
     hipLaunchKernelGGL((dkdv_kernel<T, DD, C, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
   });

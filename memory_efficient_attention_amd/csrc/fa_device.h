@@ -145,8 +145,8 @@ struct Stager {
   static constexpr int NCH = (ROWS / 4) * CS4;
   static constexpr int NINST = (NCH + 63) / 64;
   static constexpr int PER = (NINST + NW - 1) / NW;
-  int src[PER];
   int rank;   // this wave's position in the round-robin deal of instructions
+  int lane;
 
   static constexpr bool lane_active(int P) {
     return P < NCH && (P % CS4) / CS1 < 4 && (P % CS4) % CS1 < CROW;
@@ -156,7 +156,7 @@ struct Stager {
   static constexpr bool every_inst_active() {
     for (int inst = 0; inst < NINST; ++inst) {
       bool any = false;
-      for (int lane = 0; lane < 64; ++lane) any = any || lane_active(inst * 64 + lane);
+      for (int l = 0; l < 64; ++l) any = any || lane_active(inst * 64 + l);
       if (!any) return false;
     }
     return true;
@@ -166,24 +166,24 @@ struct Stager {
   // Instruction i goes to wave (first + i) % NW.  Stagers of one tile that
   // start where the previous one ended deal their instructions round-robin as
   // a single set, so every wave issues at least floor(total / NW) of them.
-  __device__ void init(int wave, int lane, int first = 0) {
+  __device__ void init(int wave, int lane_, int first = 0) {
     rank = (wave - first % NW + NW) % NW;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int P = (k * NW + rank) * 64 + lane;
-      const int g = P / CS4, w = P % CS4, b = w / CS1, c = w % CS1;
-      src[k] = lane_active(P) ? ((4 * g + b) * L::ROW + c * 16) : -1;
-    }
+    lane = lane_;
   }
 
-  // g: the (N, D) matrix of this (batch, head); N * ROW < 2^31.
+  // g: the (N, D) matrix of this (batch, head); N * ROW < 2^31.  Each lane's
+  // source offset is recomputed here (constant divisions only) rather than
+  // kept in registers across the tile walk.
   __device__ void issue(FA_LDS char* tile, const T* g, int row0, int N) const {
     const i32x4 rsrc = buffer_rsrc(g, N * L::ROW);
     const int base = row0 * L::ROW;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int inst = k * NW + rank;
-      if (inst < NINST && src[k] >= 0) buffer_lds16(rsrc, tile + inst * 1024, base + src[k]);
+      const int P = inst * 64 + lane;
+      const int grp = P / CS4, w = P % CS4, r = w / CS1, c = w % CS1;
+      if (inst < NINST && lane_active(P))
+        buffer_lds16(rsrc, tile + inst * 1024, base + (4 * grp + r) * L::ROW + c * 16);
     }
   }
 };

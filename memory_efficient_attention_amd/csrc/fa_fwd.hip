@@ -65,10 +65,13 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
     b = bh / p.H;
     kt_hi = ((CAUSAL ? min(qt * BM + BM, N) : N) - 1) / BN;
   }
+  // q and o rows of head bh; k and v of its key/value head (grouped-query
+  // heads form contiguous runs of G)
   const size_t off = (size_t)bh * N * D;
+  const size_t offkv = (size_t)(bh / p.G) * N * D;
   const T* gq = (const T*)p.q + off;
-  const T* gk = (const T*)p.k + off;
-  const T* gv = (const T*)p.v + off;
+  const T* gk = (const T*)p.k + offkv;
+  const T* gv = (const T*)p.v + offkv;
   const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
 
   // The wave owns queries qw0 .. qw0 + 31; lane l holds query qw0 + l % 32.

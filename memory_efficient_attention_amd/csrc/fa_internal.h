@@ -35,8 +35,9 @@ namespace fa {
 #endif
 // Load pipeline depth: each kernel keeps up to STAGES - 1 tiles staged ahead
 // of the one it computes on, as far as its LDS share allows.  Measured on
-// MI355X, deeper rings help only dK/dV (whose tiles are half the size); fp32
-// tiles (small shapes only) always use two stages and full waits.
+// MI355X, rings deeper than two stages gain nothing here (within 1 %), and
+// the dK/dV kernel, which runs at the 256-register limit, spills with three;
+// fp32 tiles (small shapes only) always use two stages and full waits.
 #ifndef FA_FWD_STAGES
 #define FA_FWD_STAGES 2
 #endif
@@ -44,7 +45,7 @@ namespace fa {
 #define FA_DQ_STAGES 2
 #endif
 #ifndef FA_DKV_STAGES
-#define FA_DKV_STAGES 4
+#define FA_DKV_STAGES 2
 #endif
 constexpr int WAVES_DENSE = FA_WAVES_DENSE;
 constexpr int WAVES_PACKED = FA_WAVES_PACKED;
@@ -82,6 +83,7 @@ struct FwdParams {
   // tile, longest first; workgroup w runs head w % H of entry w / H
   const int4* work;
   int B, H, N, nqt;
+  int G;                 // query heads per key/value head (H / Hkv)
   float scale;           // softmax scale
   float c;               // scale * log2(e)
 };
@@ -94,7 +96,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  const float* lse2;     // log2-domain LSE (B, H, N)
+  const float* nls;      // -LSE / scale (B, H, N)
   const float* delta;    // -D_i = -dO_i . O_i (B, H, N)
   const int32_t* seg;
   // packed only, longest first: dQ {b, query tile, first, last key tile};
@@ -102,6 +104,7 @@ struct BwdParams {
   // w % H of entry w / H
   const int4* work;
   int B, H, N, ntiles;
+  int G;                 // query heads per key/value head (H / Hkv)
   float scale, c;
 };
 
@@ -110,7 +113,8 @@ struct PreParams {
   const void* dO;
   const float* lse;
   float* delta;
-  float* lse2;
+  float* nls;
+  float scale;
   long long rows;
 };
 

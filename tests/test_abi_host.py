@@ -64,21 +64,25 @@ GOOD = dict(B=1, H=2, N=64, D=64, dtype=0, scale=0.125)
 P = 0x100000   # fake, 256-aligned, never dereferenced
 
 
-def _fwd(lib, q=P, k=P, v=P, seg=None, scale=0.125, causal=1, o=P, lse=P, B=1, H=2, N=64, D=64,
-         dtype=0, ws=None, ws_bytes=0):
-    return lib.fa_fwd(q, k, v, seg, ctypes.c_float(scale), causal, o, lse, B, H, N, D, dtype, ws,
+def _fwd(lib, q=P, k=P, v=P, seg=None, scale=0.125, causal=1, o=P, lse=P, B=1, H=2, Hkv=None,
+         N=64, D=64, dtype=0, ws=None, ws_bytes=0):
+    Hkv = H if Hkv is None else Hkv
+    return lib.fa_fwd(q, k, v, seg, ctypes.c_float(scale), causal, o, lse, B, H, Hkv, N, D, dtype, ws,
                       ws_bytes, None)
 
 
 def _bwd(lib, q=P, k=P, v=P, o=P, do=P, lse=P, seg=None, scale=0.125, causal=1, dq=P, dk=P, dv=P,
-         B=1, H=2, N=64, D=64, dtype=0, ws=P, ws_bytes=1 << 30):
-    return lib.fa_bwd(q, k, v, o, do, lse, seg, ctypes.c_float(scale), causal, dq, dk, dv, B, H, N, D,
-                      dtype, ws, ws_bytes, None)
+         B=1, H=2, Hkv=None, N=64, D=64, dtype=0, ws=P, ws_bytes=1 << 30):
+    Hkv = H if Hkv is None else Hkv
+    return lib.fa_bwd(q, k, v, o, do, lse, seg, ctypes.c_float(scale), causal, dq, dk, dv, B, H, Hkv, N,
+                      D, dtype, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), FA_ERR_NULL), (dict(lse=None), FA_ERR_NULL), (dict(o=None), FA_ERR_NULL),
     (dict(B=0), FA_ERR_SHAPE), (dict(H=-1), FA_ERR_SHAPE), (dict(N=0), FA_ERR_SHAPE),
+    (dict(Hkv=0), FA_ERR_SHAPE), (dict(Hkv=-2), FA_ERR_SHAPE), (dict(H=6, Hkv=4), FA_ERR_SHAPE),
+    (dict(H=2, Hkv=4), FA_ERR_SHAPE),
     (dict(N=(1 << 22) + 1), FA_ERR_SHAPE), (dict(N=1 << 22, D=128, dtype=1), FA_ERR_SHAPE), (dict(B=1 << 16, H=1 << 10, N=1 << 10), FA_ERR_SHAPE),
     (dict(D=96), FA_ERR_HEAD_DIM), (dict(D=32), FA_ERR_HEAD_DIM), (dict(D=256), FA_ERR_HEAD_DIM),
     (dict(dtype=2), FA_ERR_DTYPE), (dict(dtype=-1), FA_ERR_DTYPE),
@@ -95,7 +99,8 @@ def test_fwd_refusals(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(do=None), FA_ERR_NULL), (dict(dv=None), FA_ERR_NULL), (dict(lse=None), FA_ERR_NULL),
-    (dict(N=-5), FA_ERR_SHAPE), (dict(D=80), FA_ERR_HEAD_DIM), (dict(dtype=7), FA_ERR_DTYPE),
+    (dict(N=-5), FA_ERR_SHAPE), (dict(H=8, Hkv=3), FA_ERR_SHAPE), (dict(D=80), FA_ERR_HEAD_DIM),
+    (dict(dtype=7), FA_ERR_DTYPE),
     (dict(scale=float("-inf")), FA_ERR_SCALE), (dict(dk=P + 4), FA_ERR_ALIGN),
     (dict(ws=None), FA_ERR_WORKSPACE), (dict(ws_bytes=100), FA_ERR_WORKSPACE),
     (dict(ws=P + 64), FA_ERR_ALIGN),

@@ -75,6 +75,26 @@ def test_small_shapes(B, H, N, D, dtype, mode):
     _compare(out, ref, dtype)
 
 
+GQA_SHAPES = [(1, 4, 2, 129, 64), (2, 4, 1, 257, 128), (1, 6, 3, 200, 128)]
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,H,Hkv,N,D", GQA_SHAPES)
+def test_grouped_query_heads(B, H, Hkv, N, D, dtype, mode):
+    """K/V with fewer heads than Q: query head h reads key/value head
+    h // (H / Hkv), and dK/dV of a key/value head sum over its query heads."""
+    packed, causal = MODES[mode]
+    seed = 2000 + 7 * N + D + H + Hkv
+    say(f"grouped heads B{B} H{H} Hkv{Hkv} N{N} D{D} {dtype} {mode} seed {seed}")
+    t = workloads.make_tensors(B, H, N, D, dtype, seed, Hkv=Hkv)
+    seg = workloads.random_segments(B, N, seed, max_len=max(1, N // 4)) if packed else None
+    scale = 1.0 / np.sqrt(D)
+    out = run_gpu(t, seg, dtype, scale, causal)
+    assert tuple(out["dk"].shape) == (B, Hkv, N, D)
+    _compare(out, _oracle_full(t, seg, scale, causal), dtype)
+
+
 def test_short_segments_many_tiles():
     """Segments of 1..5 tokens: nearly every tile pair is cross-segment."""
     B, H, N, D = 2, 2, 700, 128
@@ -184,15 +204,19 @@ def _invariants(out, tol=1e-2, tol_dk=0.1):
     few tokens reaches a few percent of sum |dK|; tol_dk = 0.1 still fails any
     structural error (a missed or extra tile), which gives ratios of order 1."""
     seg = out["seg"]
+    B, H = out["q"].shape[:2]
+    Hkv = out["k"].shape[1]
     dk_s, dk_m = _seg_sums(out["dk"], seg)
     assert bool((dk_s.abs() <= tol_dk * dk_m + 1e-6).all()), \
         f"sum dK per segment: worst {(dk_s.abs() / (dk_m + 1e-30)).max().item():.3e}"
     dv_s, dv_m = _seg_sums(out["dv"], seg)
     do_s, _ = _seg_sums(out["do"], seg)
+    do_s = do_s.reshape(B, Hkv, H // Hkv, *do_s.shape[2:]).sum(dim=2)   # a group's query heads
     assert bool(((dv_s - do_s).abs() <= tol * dv_m + 1e-6).all()), "sum dV != sum dO per segment"
-    lhs = (out["q"].double() * out["dq"].double()).sum(dim=(2, 3))
+    qdq = (out["q"].double() * out["dq"].double()).sum(dim=(2, 3))
+    lhs = qdq.reshape(B, Hkv, H // Hkv).sum(dim=2)
     rhs = (out["k"].double() * out["dk"].double()).sum(dim=(2, 3))
-    mag = (out["q"].double() * out["dq"].double()).abs().sum(dim=(2, 3))
+    mag = (out["q"].double() * out["dq"].double()).abs().sum(dim=(2, 3)).reshape(B, Hkv, -1).sum(dim=2)
     assert bool(((lhs - rhs).abs() <= tol * mag).all()), "sum q.dQ != sum k.dK"
 
 
@@ -291,3 +315,32 @@ def test_packed_outputs_do_not_depend_on_other_segments():
     for n in ("o", "lse", "dq", "dk", "dv"):
         x, y = a[n][:, :, keep], b2[n][:, :, keep]
         assert bool((x == y).all()), f"{n} of other segments changed"
+
+
+def test_grouped_query_heads_8k():
+    """The pages' flagship attention shape: B1, 32 query / 8 key-value heads,
+    N = 8192, D = 128, causal."""
+    w = workloads.get("gqa_8k")
+    say(f"workload {w.name}: {w.note}")
+    t = w.tensors()
+    out = run_gpu(t, None, w.dtype, w.scale, True)
+    G = w.H // w.Hkv
+    g = 5
+    say(f"  oracle key/value head {g} with its {G} query heads")
+    tb = {n: (t[n][:, g:g + 1] if n in ("k", "v") else t[n][:, g * G:(g + 1) * G]) for n in t}
+    ref = _oracle_full(tb, None, w.scale, True)
+    o, lse = down(out["o"][:, g * G:(g + 1) * G]), down(out["lse"][:, g * G:(g + 1) * G])
+    check_o(o, ref["o"], w.dtype)
+    check_lse(lse, ref["lse"], w.dtype)
+    check_grad(down(out["dq"][:, g * G:(g + 1) * G]), ref["dq"], w.dtype, "dq")
+    check_grad(down(out["dk"][:, g:g + 1]), ref["dk"], w.dtype, "dk")
+    check_grad(down(out["dv"][:, g:g + 1]), ref["dv"], w.dtype, "dv")
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, w.N - 1], rng.integers(0, w.N, 11)]))
+    o_all, lse_all = down(out["o"]), down(out["lse"])
+    for hh in range(w.H):
+        o_r, l_r = attention_rows(t["q"][0, hh], t["k"][0, hh // G], t["v"][0, hh // G], rows, None,
+                                  w.scale, True)
+        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}")
+        check_lse(lse_all[0, hh, rows], l_r, w.dtype)
+    _invariants(out)

@@ -135,16 +135,18 @@ def random_segments(B: int, N: int, seed: int, max_len: int | None = None) -> np
 
 
 def make_tensors(B: int, H: int, N: int, D: int, dtype: str, seed: int,
-                 names=("q", "k", "v", "do")) -> dict[str, np.ndarray]:
-    """Q, K, V, dO as float32 (B, H, N, D), iid N(0, 1), bf16-rounded for bf16.
+                 names=("q", "k", "v", "do"), Hkv: int | None = None) -> dict[str, np.ndarray]:
+    """Q and dO as float32 (B, H, N, D), K and V as (B, Hkv, N, D) (Hkv = H
+    unless given), iid N(0, 1), bf16-rounded for bf16.
 
     The four tensors are always drawn in the order q, k, v, do from one
     generator, so asking for a subset still returns the same values.
     """
     rng = np.random.default_rng([seed, 1])
+    Hkv = H if Hkv is None else Hkv
     out = {}
     for name in ("q", "k", "v", "do"):
-        x = rng.standard_normal((B, H, N, D), dtype=np.float32)
+        x = rng.standard_normal((B, Hkv if name in ("k", "v") else H, N, D), dtype=np.float32)
         if name not in names:
             continue
         if dtype == "bf16":
@@ -167,11 +169,16 @@ class Workload:
     layout: str          # "none" (plain causal), "single" (seg = 0), "short", "long"
     seed: int
     causal: bool = True
+    hkv: int = 0         # key/value heads; 0 means H (no grouping)
     note: str = field(default="", compare=False)
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.D)
+
+    @property
+    def Hkv(self) -> int:
+        return self.hkv or self.H
 
     def seg(self) -> np.ndarray | None:
         if self.layout == "none":
@@ -185,7 +192,7 @@ class Workload:
         raise ValueError(self.layout)
 
     def tensors(self, names=("q", "k", "v", "do")) -> dict[str, np.ndarray]:
-        return make_tensors(self.B, self.H, self.N, self.D, self.dtype, self.seed, names)
+        return make_tensors(self.B, self.H, self.N, self.D, self.dtype, self.seed, names, self.Hkv)
 
     def with_(self, **kw) -> "Workload":
         d = dict(self.__dict__)
@@ -206,6 +213,8 @@ WORKLOADS = {
                                   note="B1 H32 N8192 D128 bf16, packed path with one segment"),
     "packed_long_64k": Workload("packed_long_64k", 1, 8, 65536, 64, "bf16", "long", 5,
                                 note="B1 H8 N65536 D64 bf16, documents U[1024,16384]"),
+    "gqa_8k": Workload("gqa_8k", 1, 32, 8192, 128, "bf16", "none", 6, hkv=8,
+                       note="B1 H32 (8 KV heads) N8192 D128 bf16, causal"),
 }
 
 
