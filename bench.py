@@ -283,7 +283,7 @@ def report_all(args):
     import workloads
     rows = []
     names = ["tiny_causal_fp32", "causal_2k", "packed_short_4k", "single_segment_8k", "causal_16k",
-             "packed_long_64k", "gqa_8k"]
+             "packed_long_64k", "gqa_8k", "causal_8k_d96"]
     for name in names:
         w = workloads.get(name)
         print(f"# running {name}", file=sys.stderr, flush=True)

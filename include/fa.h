@@ -14,9 +14,9 @@
  *
  * Conventions shared by every entry point:
  *   - Tensors are dense, contiguous, row-major (B, H, N, D) device buffers of
- *     the element type `dtype` (bf16 or fp32), D in {64, 128}, as in the
+ *     the element type `dtype` (bf16 or fp32), D in {64, 96, 128}, as in the
  *     README's "If you maintain a trainer" section ((B, H, N, D) with head_dim
- *     in {64, 96, 128}; 96 is not built yet and is refused).
+ *     in {64, 96, 128}).
  *   - Grouped-query heads (same section: grouped query heads mapped
  *     contiguously): k, v, dk and dv have Hkv heads, H a multiple of Hkv, and
  *     query head h reads key/value head h / (H / Hkv).  Hkv = H is plain
@@ -60,7 +60,7 @@ typedef enum fa_status {
     FA_ERR_NULL = 1,       /* a required pointer is NULL */
     FA_ERR_SHAPE = 2,      /* B, H, Hkv or N < 1, H not a multiple of Hkv, or sizes
                               beyond the supported range */
-    FA_ERR_HEAD_DIM = 3,   /* D not in {64, 128} */
+    FA_ERR_HEAD_DIM = 3,   /* D not in {64, 96, 128} */
     FA_ERR_DTYPE = 4,      /* dtype is neither FA_BF16 nor FA_FP32 (fp16 is refused) */
     FA_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than fa_workspace_bytes() */
     FA_ERR_ALIGN = 6,      /* a pointer violates the alignment rules above */

@@ -92,7 +92,7 @@ fa_status device_ok() {
 
 fa_status common_checks(int B, int H, int Hkv, int N, int D, fa_dtype dtype, float scale) {
   if (!shape_ok(B, H, N) || Hkv < 1 || H % Hkv != 0) return FA_ERR_SHAPE;
-  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 64 && D != 96 && D != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_DTYPE;
   // one head's (N, D) matrix is addressed with 32-bit byte offsets
   if ((long long)N * D * (dtype == FA_FP32 ? 4 : 2) >= (1LL << 31)) return FA_ERR_SHAPE;
@@ -105,7 +105,7 @@ float log2e_scale(float scale) { return (float)((double)scale * 1.44269504088896
 }  // namespace
 
 FA_API size_t fa_workspace_bytes(int B, int H, int N, int D, int has_seg, int for_bwd) {
-  if (!shape_ok(B, H, N) || (D != 64 && D != 128)) return 0;
+  if (!shape_ok(B, H, N) || (D != 64 && D != 96 && D != 128)) return 0;
   return layout(B, H, N, has_seg != 0, for_bwd != 0).total;
 }
 
@@ -140,7 +140,7 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   p.H = H;
   p.G = H / Hkv;
   p.N = N;
-  const int nw = fa::waves_for(seg != nullptr);
+  const int nw = fa::tile_config(seg != nullptr, Hkv != H).nw_q;
   const int bm = nw * 32;   // queries per workgroup
   p.nqt = (N + bm - 1) / bm;
   p.scale = scale;
@@ -184,10 +184,8 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   float* delta = (float*)(w + L.delta);
   float* nls = (float*)(w + L.nls);
 
-  // dQ: waves per workgroup by masking; dK/dV: grouped heads divide its
-  // workgroups by H / Hkv, so it uses the smaller workgroups there too.
-  const int nw = fa::waves_for(seg != nullptr);
-  const int nw_kv = fa::waves_for(seg != nullptr || Hkv != H);
+  const fa::TileConfig cfg = fa::tile_config(seg != nullptr, Hkv != H);
+  const int nw = cfg.nw_q, nw_kv = cfg.nw_kv;
   const int bt = nw * 32;   // queries per dQ workgroup
   const int ntiles = (N + bt - 1) / bt;
   const int ntiles_kv = (N + nw_kv * 32 - 1) / (nw_kv * 32);

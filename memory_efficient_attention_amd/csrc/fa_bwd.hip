@@ -23,27 +23,34 @@ namespace fa {
 // scale: both negated so that the dK/dV kernel can start its dP and S
 // accumulators from them (dP - D_i and S - LSE / scale come straight out of
 // the MFMAs) and the dQ kernel adds them.
-// LPR lanes share one row, each reading 16 contiguous bytes of O and dO.
+// LPR lanes share one row (LPR a power of two, so a row never straddles a
+// wave), each reading VPL 16-byte vectors of O and dO.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
-  constexpr int LPR = D * (int)sizeof(T) / 16;
+  constexpr int NV = D * (int)sizeof(T) / 16;             // 16-byte vectors per row
+  constexpr int LPR = NV & -NV;                           // largest power of two dividing NV
+  constexpr int VPL = NV / LPR;
+  constexpr int EV = 16 / (int)sizeof(T);                 // elements per vector
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gid / LPR;
   const int sub = (int)(gid % LPR);
   float acc = 0.f;
   if (row < p.rows) {
-    const size_t e = (size_t)row * D + (size_t)sub * (16 / sizeof(T));
-    if constexpr (sizeof(T) == 2) {
-      const bf16x8 o = *(const bf16x8*)((const T*)p.o + e);
-      const bf16x8 g = *(const bf16x8*)((const T*)p.dO + e);
-      const f32x8 of = __builtin_convertvector(o, f32x8), gf = __builtin_convertvector(g, f32x8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc = fmaf(of[i], gf[i], acc);
-    } else {
-      const f32x4 o = *(const f32x4*)((const T*)p.o + e);
-      const f32x4 g = *(const f32x4*)((const T*)p.dO + e);
+    for (int u = 0; u < VPL; ++u) {
+      const size_t e = (size_t)row * D + (size_t)(u * LPR + sub) * EV;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 o = *(const bf16x8*)((const T*)p.o + e);
+        const bf16x8 g = *(const bf16x8*)((const T*)p.dO + e);
+        const f32x8 of = __builtin_convertvector(o, f32x8), gf = __builtin_convertvector(g, f32x8);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = fmaf(o[i], g[i], acc);
+        for (int i = 0; i < 8; ++i) acc = fmaf(of[i], gf[i], acc);
+      } else {
+        const f32x4 o = *(const f32x4*)((const T*)p.o + e);
+        const f32x4 g = *(const f32x4*)((const T*)p.dO + e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(o[i], g[i], acc);
+      }
     }
   }
 #pragma unroll
@@ -463,7 +470,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
 // ---------------------------------------------------------------- launchers
 template <typename T, int D>
 static hipError_t launch_pre_t(const PreParams& p, hipStream_t s) {
-  constexpr int LPR = D * (int)sizeof(T) / 16;
+  constexpr int NV = D * (int)sizeof(T) / 16;
+  constexpr int LPR = NV & -NV;
   const long long threads = p.rows * LPR;
   const long long blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, p);
@@ -471,8 +479,12 @@ static hipError_t launch_pre_t(const PreParams& p, hipStream_t s) {
 }
 
 hipError_t launch_bwd_pre(const PreParams& p, int dtype, int D, hipStream_t s) {
-  if (dtype == 0) return D == 128 ? launch_pre_t<bf16, 128>(p, s) : launch_pre_t<bf16, 64>(p, s);
-  return D == 128 ? launch_pre_t<float, 128>(p, s) : launch_pre_t<float, 64>(p, s);
+  if (dtype == 0) {
+    if (D == 128) return launch_pre_t<bf16, 128>(p, s);
+    return D == 96 ? launch_pre_t<bf16, 96>(p, s) : launch_pre_t<bf16, 64>(p, s);
+  }
+  if (D == 128) return launch_pre_t<float, 128>(p, s);
+  return D == 96 ? launch_pre_t<float, 96>(p, s) : launch_pre_t<float, 64>(p, s);
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s) {

@@ -79,13 +79,18 @@ __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32);
 //    apart.
 //  * row-only (frag_row only): S1 = row + 16 bytes, S4 = 4 * S1, i.e. a plain
 //    padded stride; 26 % smaller than DUAL at D = 128.
+//  * D = 96: S1 = row, S4 = 4 * row + 16 for both (checked the same way).
 // Every fragment address is a per-lane base plus a compile-time offset.  fp32
 // tiles (small shapes only) are packed without padding.
 template <typename T, int D, bool DUAL = true>
 struct Layout {
   static constexpr int ROW = D * (int)sizeof(T);
-  static constexpr int S1 = sizeof(T) == 2 ? ROW + (DUAL ? 64 : 16) : ROW;
-  static constexpr int S4 = sizeof(T) == 2 && DUAL ? 4 * S1 + 16 : 4 * S1;
+  // D = 96 (192-byte rows): S1 = row, S4 = 4 * row + 16 serves both read
+  // patterns without conflicts, so both tile kinds use it.
+  static constexpr int PAD1 = D == 96 ? 0 : (DUAL ? 64 : 16);
+  static constexpr int PAD4 = D == 96 || DUAL ? 16 : 0;
+  static constexpr int S1 = sizeof(T) == 2 ? ROW + PAD1 : ROW;
+  static constexpr int S4 = sizeof(T) == 2 ? 4 * S1 + PAD4 : 4 * S1;
   static constexpr int bytes(int rows) { return (rows / 4) * S4; }
   // byte offset of a row; linear in (row / 4, row % 4), so off(a + b) =
   // off(a) + off(b) whenever a is a multiple of 4

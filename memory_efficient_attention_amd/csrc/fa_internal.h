@@ -54,7 +54,25 @@ constexpr int QRY_TILE = FA_QRY_TILE;
 constexpr int LDS_PER_CU = 163840;
 constexpr int WAVES_PER_CU = 4 * FA_WAVES_PER_EU;
 
-constexpr int waves_for(bool packed) { return packed ? WAVES_PACKED : WAVES_DENSE; }
+// Tile configuration by shape class: waves per workgroup of the forward and
+// dQ (nw_q) and of dK/dV (nw_kv).  Where the mlx-train-perf README ("Turning
+// it on", "Training packed") calibrates its kernels with a host-synced timing
+// probe cached per batch size and sequence bucket, this is a fixed table,
+// measured offline on MI355X: calls are deterministic and capturable, and no
+// probe runs.  Every wave does the same arithmetic whatever the entry, so a
+// packed call with a single segment gives the causal call's bits.
+//   dense (causal or full), multi-head: 8 / 8 waves
+//   packed:                             4 / 4 waves (short segments, many
+//                                       small workgroups per CU)
+//   dense, grouped-query heads:         8 / 4 waves (dK/dV has H/Hkv times
+//                                       fewer workgroups; two per CU pair heavy
+//                                       and light causal key tiles)
+struct TileConfig {
+  int nw_q, nw_kv;
+};
+constexpr TileConfig tile_config(bool packed, bool grouped) {
+  return {packed ? WAVES_PACKED : WAVES_DENSE, packed || grouped ? WAVES_PACKED : WAVES_DENSE};
+}
 
 // Stages a kernel of NW waves uses: the requested depth, reduced to what
 // fits its share of the CU's LDS (WAVES_PER_CU / NW workgroups share a CU)
@@ -138,7 +156,10 @@ hipError_t dispatch(int dtype, int D, bool causal, int nw, F&& f) {
   auto by_causal = [&](auto t, auto d) {
     return causal ? by_nw(t, d, bool_c<true>{}) : by_nw(t, d, bool_c<false>{});
   };
-  auto by_d = [&](auto t) { return D == 128 ? by_causal(t, int_c<128>{}) : by_causal(t, int_c<64>{}); };
+  auto by_d = [&](auto t) {
+    if (D == 128) return by_causal(t, int_c<128>{});
+    return D == 96 ? by_causal(t, int_c<96>{}) : by_causal(t, int_c<64>{});
+  };
   return dtype == 0 ? by_d(type_c<__bf16>{}) : by_d(type_c<float>{});
 }
 // Per-tile range tables from segment ids (see fa_sched.hip).

@@ -84,7 +84,8 @@ def _bwd(lib, q=P, k=P, v=P, o=P, do=P, lse=P, seg=None, scale=0.125, causal=1, 
     (dict(Hkv=0), FA_ERR_SHAPE), (dict(Hkv=-2), FA_ERR_SHAPE), (dict(H=6, Hkv=4), FA_ERR_SHAPE),
     (dict(H=2, Hkv=4), FA_ERR_SHAPE),
     (dict(N=(1 << 22) + 1), FA_ERR_SHAPE), (dict(N=1 << 22, D=128, dtype=1), FA_ERR_SHAPE), (dict(B=1 << 16, H=1 << 10, N=1 << 10), FA_ERR_SHAPE),
-    (dict(D=96), FA_ERR_HEAD_DIM), (dict(D=32), FA_ERR_HEAD_DIM), (dict(D=256), FA_ERR_HEAD_DIM),
+    (dict(D=80), FA_ERR_HEAD_DIM), (dict(D=32), FA_ERR_HEAD_DIM), (dict(D=256), FA_ERR_HEAD_DIM),
+    (dict(D=112), FA_ERR_HEAD_DIM), (dict(D=0), FA_ERR_HEAD_DIM),
     (dict(dtype=2), FA_ERR_DTYPE), (dict(dtype=-1), FA_ERR_DTYPE),
     (dict(scale=float("nan")), FA_ERR_SCALE), (dict(scale=float("inf")), FA_ERR_SCALE),
     (dict(scale=0.0), FA_ERR_SCALE), (dict(scale=-1.0), FA_ERR_SCALE),
@@ -112,14 +113,15 @@ def test_bwd_refusals(lib, kw, status):
 def test_first_failing_check_wins(lib):
     # a null pointer is reported before a bad shape, a bad shape before a bad dtype
     assert _fwd(lib, q=None, B=0, dtype=9) == FA_ERR_NULL
-    assert _fwd(lib, B=0, D=96, dtype=9) == FA_ERR_SHAPE
-    assert _fwd(lib, D=96, dtype=9) == FA_ERR_HEAD_DIM
+    assert _fwd(lib, B=0, D=80, dtype=9) == FA_ERR_SHAPE
+    assert _fwd(lib, D=80, dtype=9) == FA_ERR_HEAD_DIM
 
 
 def test_workspace_sizes(lib):
     ws = lib.fa_workspace_bytes
     assert ws(1, 32, 16384, 128, 0, 0) == 0                    # plain forward needs none
-    assert ws(0, 1, 1, 64, 0, 1) == 0 and ws(1, 1, 1, 96, 0, 1) == 0
+    assert ws(0, 1, 1, 64, 0, 1) == 0 and ws(1, 1, 1, 80, 0, 1) == 0
+    assert ws(1, 1, 1, 96, 0, 1) == 256 + 2 * 256                # head_dim 96 is supported
     b1 = ws(1, 32, 8192, 128, 0, 1)
     b2 = ws(1, 32, 16384, 128, 0, 1)
     # O(N): two fp32 (B,H,N) arrays plus a 256-byte flag block

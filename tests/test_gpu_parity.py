@@ -55,7 +55,7 @@ def _compare(out, ref, dtype, sl=(slice(None),), tag=""):
 # ---------------------------------------------------------------- small shapes
 
 SHAPES = [(1, 2, 1, 64), (1, 1, 17, 64), (2, 2, 255, 128), (1, 2, 257, 64), (1, 3, 300, 128),
-          (2, 1, 129, 128)]
+          (2, 1, 129, 128), (1, 2, 200, 96), (2, 1, 65, 96)]
 MODES = {"causal": (False, True), "packed": (True, True), "packed_bidir": (True, False),
          "full": (False, False)}
 
@@ -75,7 +75,7 @@ def test_small_shapes(B, H, N, D, dtype, mode):
     _compare(out, ref, dtype)
 
 
-GQA_SHAPES = [(1, 4, 2, 129, 64), (2, 4, 1, 257, 128), (1, 6, 3, 200, 128)]
+GQA_SHAPES = [(1, 4, 2, 129, 64), (2, 4, 1, 257, 128), (1, 6, 3, 200, 128), (1, 4, 2, 150, 96)]
 
 
 @pytest.mark.parametrize("mode", list(MODES))
@@ -341,6 +341,28 @@ def test_grouped_query_heads_8k():
     for hh in range(w.H):
         o_r, l_r = attention_rows(t["q"][0, hh], t["k"][0, hh // G], t["v"][0, hh // G], rows, None,
                                   w.scale, True)
+        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}")
+        check_lse(lse_all[0, hh, rows], l_r, w.dtype)
+    _invariants(out)
+
+
+def test_head_dim_96_8k():
+    """head_dim 96 at a full-size causal shape: one whole head against the
+    oracle, sampled rows of every head, and the identities."""
+    w = workloads.get("causal_8k_d96")
+    say(f"workload {w.name}: {w.note}")
+    t = w.tensors()
+    out = run_gpu(t, None, w.dtype, w.scale, True)
+    b, h = 0, 11
+    say(f"  oracle head b{b} h{h}")
+    tb = {n: t[n][b:b + 1, h:h + 1] for n in t}
+    _compare(out, _oracle_full(tb, None, w.scale, True), w.dtype, (slice(b, b + 1), slice(h, h + 1)),
+             f"[b{b} h{h}]")
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, w.N - 1], rng.integers(0, w.N, 11)]))
+    o_all, lse_all = down(out["o"]), down(out["lse"])
+    for hh in range(w.H):
+        o_r, l_r = attention_rows(t["q"][0, hh], t["k"][0, hh], t["v"][0, hh], rows, None, w.scale, True)
         check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}")
         check_lse(lse_all[0, hh, rows], l_r, w.dtype)
     _invariants(out)

@@ -215,6 +215,8 @@ WORKLOADS = {
                                 note="B1 H8 N65536 D64 bf16, documents U[1024,16384]"),
     "gqa_8k": Workload("gqa_8k", 1, 32, 8192, 128, "bf16", "none", 6, hkv=8,
                        note="B1 H32 (8 KV heads) N8192 D128 bf16, causal"),
+    "causal_8k_d96": Workload("causal_8k_d96", 1, 32, 8192, 96, "bf16", "none", 7,
+                              note="B1 H32 N8192 D96 bf16, causal"),
 }
 
 
