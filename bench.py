@@ -279,6 +279,51 @@ def headline(args):
     print(json.dumps(out), flush=True)
 
 
+def run_lce(steps, warmup):
+    """Time the fused linear cross-entropy at the pages' loss-layer shape
+    (N = 8192, V = 151936, D = 4096, bf16): fa_lce_fwd, then fa_lce_bwd with
+    dh and dW, each bracketed by HIP events on the current stream."""
+    import torch
+    import workloads
+    import memory_efficient_attention_amd as fa
+    c = workloads.LCE_WORKLOAD
+    N, V, D = c["N"], c["V"], c["D"]
+    print(f"# generating {c['name']} inputs", file=sys.stderr, flush=True)
+    x = workloads.make_lce_inputs(N, V, D, c["seed"])
+    h = torch.from_numpy(x["h"]).cuda().to(torch.bfloat16)
+    w = torch.from_numpy(x["w"]).cuda().to(torch.bfloat16)
+    del x["w"]
+    t = torch.from_numpy(x["targets"]).cuda()
+    g = torch.from_numpy(x["dnll"]).cuda()
+    ws_f = torch.empty(fa.fa_lce_workspace_bytes(N, V, D, False), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(fa.fa_lce_workspace_bytes(N, V, D, True), dtype=torch.uint8, device="cuda")
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    lse = None
+    for _ in range(warmup):
+        _, lse, _ = fa.fa_lce_fwd(h, w, t, workspace=ws_f)
+        fa.fa_lce_bwd(h, w, t, lse, g, workspace=ws_b)
+    E = [[ev.new() for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in E:
+        ev.record(e[0], stream)
+        _, lse, _ = fa.fa_lce_fwd(h, w, t, workspace=ws_f)
+        ev.record(e[1], stream)
+        fa.fa_lce_bwd(h, w, t, lse, g, workspace=ws_b)
+        ev.record(e[2], stream)
+    torch.cuda.synchronize()
+    fwd = sum(ev.ms(e[0], e[1]) for e in E) / steps
+    bwd = sum(ev.ms(e[1], e[2]) for e in E) / steps
+    ev.close()
+    flop = 2.0 * N * V * D
+    return {"workload": c["name"], "fwd_ms": round(fwd, 3), "bwd_ms": round(bwd, 3),
+            "fwd_tflops": round(flop / (fwd * 1e-3) / 1e12, 1),
+            # backward: logits recomputed, dh = dZ W, dW = dZ^T H
+            "bwd_tflops": round(3 * flop / (bwd * 1e-3) / 1e12, 1),
+            "workspace_bytes": {"fwd": ws_f.numel(), "bwd": ws_b.numel()},
+            "logits_bytes_bf16": N * V * 2}
+
+
 def report_all(args):
     import workloads
     rows = []
@@ -384,6 +429,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="table over every workload instead of the JSON line")
+    ap.add_argument("--lce", action="store_true", help="time the fused linear cross-entropy loss layer")
     ap.add_argument("--copy-calibration", action="store_true", help="plain copy of known size for counters")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
                                                            "CAL_WRITE_DIR"),
@@ -405,6 +451,8 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+    elif args.lce:
+        print(json.dumps(run_lce(args.steps, args.warmup)), flush=True)
     elif args.all:
         report_all(args)
     else:

@@ -155,6 +155,45 @@ fa_status fa_check_seg(const int32_t* host_seg, int B, int N);
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status status);
 
+/*
+ * Fused linear cross-entropy: the loss layer of a language model without the
+ * (N, V) logits tensor (mlx-train-perf README, section "The fused
+ * cross-entropy loss": the forward regenerates the logits tile by tile and
+ * returns the per-token NLL, log-sum-exp and target logit; the backward
+ * recomputes the tiles it needs).  Logits are Z = h w^T, accumulated in fp32.
+ *   h       : (N, D) bf16 hidden states; w : (V, D) bf16 dense output head.
+ *   targets : (N,) int32, each in [0, V) (an id outside gives unspecified
+ *             values for that token; every access stays in bounds).
+ * bf16 only (FA_ERR_DTYPE otherwise); D a multiple of 256, and V * D, N * D
+ * and N * FA_LCE_VOCAB_CHUNK elements below 2^30 (FA_ERR_SHAPE otherwise).
+ * The backward walks the vocabulary in chunks of FA_LCE_VOCAB_CHUNK rows.
+ * Same alignment, ownership, stream and refusal rules as the attention calls
+ * (4-byte alignment for targets and the fp32 arrays).
+ */
+#define FA_LCE_VOCAB_CHUNK 8192
+
+/* Workspace bytes of fa_lce_fwd (for_bwd = 0) or fa_lce_bwd (for_bwd = 1):
+ * forward ceil(V/256) * N float pairs (per-tile partial maxima and sums);
+ * backward an (N, FA_LCE_VOCAB_CHUNK) bf16 dZ chunk plus, when V spans more
+ * than one chunk, an (N, D) fp32 dh accumulator.  0 for refused shapes. */
+size_t fa_lce_workspace_bytes(int N, int V, int D, int for_bwd);
+
+/* Forward: nll[i] = lse[i] - tlogit[i], lse[i] = ln sum_v exp(Z[i][v]),
+ * tlogit[i] = Z[i][targets[i]]; all (N,) fp32, written. */
+fa_status fa_lce_fwd(const void* h, const void* w, const int32_t* targets,
+                     float* nll, float* lse, float* tlogit,
+                     int N, int V, int D, fa_dtype dtype,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Backward from dnll (N,) fp32, the gradient of the loss with respect to
+ * each token's NLL (1/N for a mean): with dZ = dnll[i] (softmax(Z[i]) -
+ * onehot(targets[i])), writes dh = dZ w (N, D) bf16 and, when dw is not NULL,
+ * dw = dZ^T h (V, D) bf16.  lse is the forward's. */
+fa_status fa_lce_bwd(const void* h, const void* w, const int32_t* targets,
+                     const float* lse, const float* dnll, void* dh, void* dw,
+                     int N, int V, int D, fa_dtype dtype,
+                     void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

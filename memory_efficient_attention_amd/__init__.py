@@ -1,15 +1,19 @@
 """Python binding of the gfx950 O(N)-memory attention library (libfa.so).
 
-Argument marshalling only: every step of the attention runs in the library's
-HIP kernels.  PyTorch provides device memory (output and workspace tensors)
-and the current HIP stream.  The functions carry the C entry points' names:
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory (output and workspace tensors) and the current
+HIP stream.  The functions carry the C entry points' names:
 
     o, lse = fa_fwd(q, k, v, seg=None, scale=None, causal=True)
     dq, dk, dv = fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True)
+    nll, lse, tlogit = fa_lce_fwd(h, w, targets)
+    dh, dw = fa_lce_bwd(h, w, targets, lse, dnll)
 
-q, k, v, o, do are contiguous (B, H, N, D) CUDA tensors (torch.bfloat16 or
-torch.float32, D in {64, 128}); seg is None or a contiguous (B, N) int32 CUDA
-tensor of non-decreasing segment ids; lse is (B, H, N) float32.  A refused
+q, o, do are contiguous (B, H, N, D) CUDA tensors and k, v (B, Hkv, N, D)
+with Hkv dividing H (torch.bfloat16 or torch.float32, D in {64, 96, 128}); seg
+is None or a contiguous (B, N) int32 CUDA tensor of non-decreasing segment
+ids; lse is (B, H, N) float32.  The fused linear cross-entropy takes bf16
+hidden states h (N, D) and head w (V, D) and int32 targets (N,).  A refused
 call raises FaError naming the reason; there is no fallback path.
 """
 from __future__ import annotations
@@ -19,8 +23,8 @@ import math
 import os
 
 __all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_workspace_bytes", "fa_check_seg",
-           "fa_status_string", "flash_attention", "library_path", "load_library",
-           "FA_BF16", "FA_FP32"]
+           "fa_status_string", "flash_attention", "fa_lce_fwd", "fa_lce_bwd", "fa_lce_workspace_bytes",
+           "linear_cross_entropy", "library_path", "load_library", "FA_BF16", "FA_FP32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
@@ -64,6 +68,12 @@ def load_library():
     lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp,
                                  vp]
     lib.fa_bwd_timed.restype = i
+    lib.fa_lce_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_lce_workspace_bytes.restype = sz
+    lib.fa_lce_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_lce_fwd.restype = i
+    lib.fa_lce_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_lce_bwd.restype = i
     lib.fa_check_seg.argtypes = [vp, i, i]
     lib.fa_check_seg.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -219,3 +229,83 @@ def flash_attention(q, k, v, scale=None, causal=True, segments=None):
             return fa_bwd(q_, k_, v_, o, do.contiguous(), lse, segments, scale, causal)
 
     return _Fn.apply(q, k, v)
+
+
+# ---------------------------------------------------------------- linear cross-entropy
+
+def fa_lce_workspace_bytes(N: int, V: int, D: int, for_bwd: bool) -> int:
+    return int(load_library().fa_lce_workspace_bytes(N, V, D, int(bool(for_bwd))))
+
+
+def fa_lce_fwd(h, w, targets, workspace=None):
+    """Fused linear cross-entropy forward; returns (nll, lse, tlogit), each (N,)
+    fp32.  h (N, D) and w (V, D) bf16, targets (N,) int32."""
+    import torch
+    N, D = h.shape
+    V = w.shape[0]
+    _check_tensor("h", h, (N, D), h.dtype)
+    _check_tensor("w", w, (V, D), h.dtype)
+    _check_tensor("targets", targets, (N,), torch.int32)
+    nll, lse, tz = (torch.empty(N, dtype=torch.float32, device=h.device) for _ in range(3))
+    lib = load_library()
+    nbytes = lib.fa_lce_workspace_bytes(N, V, D, 0)
+    ws = workspace
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=h.device)
+    st = lib.fa_lce_fwd(h.data_ptr(), w.data_ptr(), targets.data_ptr(), nll.data_ptr(), lse.data_ptr(),
+                        tz.data_ptr(), N, V, D, _dtype_code(h), ws.data_ptr(), ws.numel(), _stream())
+    if st:
+        raise FaError(st, "fa_lce_fwd")
+    return nll, lse, tz
+
+
+def fa_lce_bwd(h, w, targets, lse, dnll, need_dw=True, workspace=None):
+    """Backward from per-token NLL gradients dnll (N,) fp32; returns (dh, dw)
+    (dw is None when need_dw is False)."""
+    import torch
+    N, D = h.shape
+    V = w.shape[0]
+    _check_tensor("h", h, (N, D), h.dtype)
+    _check_tensor("w", w, (V, D), h.dtype)
+    _check_tensor("targets", targets, (N,), torch.int32)
+    _check_tensor("lse", lse, (N,), torch.float32)
+    _check_tensor("dnll", dnll, (N,), torch.float32)
+    dh = torch.empty_like(h)
+    dw = torch.empty_like(w) if need_dw else None
+    lib = load_library()
+    nbytes = lib.fa_lce_workspace_bytes(N, V, D, 1)
+    ws = workspace
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=h.device)
+    st = lib.fa_lce_bwd(h.data_ptr(), w.data_ptr(), targets.data_ptr(), lse.data_ptr(), dnll.data_ptr(),
+                        dh.data_ptr(), dw.data_ptr() if dw is not None else None, N, V, D, _dtype_code(h),
+                        ws.data_ptr(), ws.numel(), _stream())
+    if st:
+        raise FaError(st, "fa_lce_bwd")
+    return dh, dw
+
+
+def linear_cross_entropy(h, w, targets, reduction="mean"):
+    """Differentiable loss through fa_lce_fwd / fa_lce_bwd: NLL of
+    softmax(h w^T) at `targets`, reduced by "mean", "sum" or "none"."""
+    import torch
+    if reduction not in ("mean", "sum", "none"):
+        raise ValueError(f"reduction {reduction!r}")
+
+    class _Fn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, h_, w_):
+            nll, lse, _ = fa_lce_fwd(h_, w_, targets)
+            ctx.save_for_backward(h_, w_, lse)
+            return nll
+
+        @staticmethod
+        def backward(ctx, g):
+            h_, w_, lse = ctx.saved_tensors
+            dh, dw = fa_lce_bwd(h_, w_, targets, lse, g.contiguous().float(), need_dw=ctx.needs_input_grad[1])
+            return dh, dw
+
+    nll = _Fn.apply(h, w)
+    if reduction == "mean":
+        return nll.mean()
+    return nll.sum() if reduction == "sum" else nll

@@ -261,6 +261,102 @@ FA_API fa_status fa_bwd_timed(const void* q, const void* k, const void* v, const
                   stream, events);
 }
 
+// ---------------------------------------------------------------- linear cross-entropy
+namespace {
+
+struct LceLayout {
+  size_t part = 0, dz = 0, dh32 = 0, total = 0;
+};
+
+fa_status lce_checks(int N, int V, int D, fa_dtype dtype) {
+  if (N < 1 || V < 1 || D < 1) return FA_ERR_SHAPE;
+  if (D % 256 != 0) return FA_ERR_SHAPE;
+  const long long lim = 1LL << 30;
+  if ((long long)V * D >= lim || (long long)N * D >= lim || (long long)N * FA_LCE_VOCAB_CHUNK >= lim)
+    return FA_ERR_SHAPE;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  return FA_OK;
+}
+
+LceLayout lce_layout(int N, int V, int D, bool for_bwd) {
+  LceLayout L;
+  if (!for_bwd) {
+    L.part = 0;
+    L.total = align_up((size_t)((V + 255) / 256) * N * 2 * sizeof(float));
+    return L;
+  }
+  L.dz = 0;
+  size_t off = align_up((size_t)N * FA_LCE_VOCAB_CHUNK * 2);
+  L.dh32 = off;
+  if (V > FA_LCE_VOCAB_CHUNK) off += align_up((size_t)N * D * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+FA_API size_t fa_lce_workspace_bytes(int N, int V, int D, int for_bwd) {
+  if (lce_checks(N, V, D, FA_BF16) != FA_OK) return 0;
+  return lce_layout(N, V, D, for_bwd != 0).total;
+}
+
+FA_API fa_status fa_lce_fwd(const void* h, const void* w, const int32_t* targets, float* nll, float* lse,
+                            float* tlogit, int N, int V, int D, fa_dtype dtype, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!h || !w || !targets || !nll || !lse || !tlogit) return FA_ERR_NULL;
+  if (fa_status st = lce_checks(N, V, D, dtype)) return st;
+  if (!aligned(h, 16) || !aligned(w, 16) || !aligned(targets, 4) || !aligned(nll, 4) || !aligned(lse, 4) ||
+      !aligned(tlogit, 4))
+    return FA_ERR_ALIGN;
+  const LceLayout L = lce_layout(N, V, D, false);
+  if (!ws || ws_bytes < L.total) return FA_ERR_WORKSPACE;
+  if (!aligned(ws, kAlign)) return FA_ERR_ALIGN;
+  if (fa_status st = device_ok()) return st;
+  (void)hipGetLastError();
+  fa::LceParams p{};
+  p.h = h;
+  p.w = w;
+  p.targets = targets;
+  p.nll = nll;
+  p.lse = lse;
+  p.tlogit = tlogit;
+  p.part = (float*)((char*)ws + L.part);
+  p.N = N;
+  p.V = V;
+  p.D = D;
+  return fa::launch_lce_fwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+FA_API fa_status fa_lce_bwd(const void* h, const void* w, const int32_t* targets, const float* lse,
+                            const float* dnll, void* dh, void* dw, int N, int V, int D, fa_dtype dtype,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !w || !targets || !lse || !dnll || !dh) return FA_ERR_NULL;
+  if (fa_status st = lce_checks(N, V, D, dtype)) return st;
+  if (!aligned(h, 16) || !aligned(w, 16) || !aligned(dh, 16) || !aligned(dw, 16) || !aligned(targets, 4) ||
+      !aligned(lse, 4) || !aligned(dnll, 4))
+    return FA_ERR_ALIGN;
+  const LceLayout L = lce_layout(N, V, D, true);
+  if (!ws || ws_bytes < L.total) return FA_ERR_WORKSPACE;
+  if (!aligned(ws, kAlign)) return FA_ERR_ALIGN;
+  if (fa_status st = device_ok()) return st;
+  (void)hipGetLastError();
+  fa::LceParams p{};
+  p.h = h;
+  p.w = w;
+  p.targets = targets;
+  p.lse_in = lse;
+  p.dnll = dnll;
+  p.dz = (char*)ws + L.dz;
+  p.dh32 = (float*)((char*)ws + L.dh32);
+  p.dh = dh;
+  p.dw = dw;
+  p.N = N;
+  p.V = V;
+  p.D = D;
+  return fa::launch_lce_bwd(p, FA_LCE_VOCAB_CHUNK, (hipStream_t)stream, nullptr) == hipSuccess ? FA_OK
+                                                                                             : FA_ERR_HIP;
+}
+
 FA_API fa_status fa_check_seg(const int32_t* host_seg, int B, int N) {
   if (!host_seg) return FA_ERR_NULL;
   if (B < 1 || N < 1 || N > FA_MAX_N) return FA_ERR_SHAPE;

@@ -85,10 +85,12 @@ __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32);
 template <typename T, int D, bool DUAL = true>
 struct Layout {
   static constexpr int ROW = D * (int)sizeof(T);
-  // D = 96 (192-byte rows): S1 = row, S4 = 4 * row + 16 serves both read
-  // patterns without conflicts, so both tile kinds use it.
-  static constexpr int PAD1 = D == 96 ? 0 : (DUAL ? 64 : 16);
-  static constexpr int PAD4 = D == 96 || DUAL ? 16 : 0;
+  // D = 96 (192-byte rows) and D = 32 (64-byte rows, the K-slices of the
+  // loss GEMMs): S1 = row, S4 = 4 * row + 16 serves every read pattern
+  // without conflicts, so both tile kinds use it.
+  static constexpr bool TIGHT = D == 96 || D == 32;
+  static constexpr int PAD1 = TIGHT ? 0 : (DUAL ? 64 : 16);
+  static constexpr int PAD4 = TIGHT || DUAL ? 16 : 0;
   static constexpr int S1 = sizeof(T) == 2 ? ROW + PAD1 : ROW;
   static constexpr int S4 = sizeof(T) == 2 ? 4 * S1 + PAD4 : 4 * S1;
   static constexpr int bytes(int rows) { return (rows / 4) * S4; }
@@ -180,15 +182,22 @@ struct Stager {
   // source offset is recomputed here (constant divisions only) rather than
   // kept in registers across the tile walk.
   __device__ void issue(FA_LDS char* tile, const T* g, int row0, int N) const {
-    const i32x4 rsrc = buffer_rsrc(g, N * L::ROW);
-    const int base = row0 * L::ROW;
+    issue_block(tile, g, row0, N, L::ROW, 0);
+  }
+  // Rows row0 .. row0 + ROWS - 1, bytes col_byte0 .. col_byte0 + ROW - 1 of
+  // each, of a row-major matrix of `nrows` rows, `ld_bytes` apart
+  // (nrows * ld_bytes < 2^31); rows past nrows read as zeros.
+  __device__ void issue_block(FA_LDS char* tile, const void* g, int row0, int nrows, int ld_bytes,
+                              int col_byte0) const {
+    const i32x4 rsrc = buffer_rsrc(g, nrows * ld_bytes);
+    const int base = row0 * ld_bytes + col_byte0;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int inst = k * NW + rank;
       const int P = inst * 64 + lane;
       const int grp = P / CS4, w = P % CS4, r = w / CS1, c = w % CS1;
       if (inst < NINST && lane_active(P))
-        buffer_lds16(rsrc, tile + inst * 1024, base + (4 * grp + r) * L::ROW + c * 16);
+        buffer_lds16(rsrc, tile + inst * 1024, base + (4 * grp + r) * ld_bytes + c * 16);
     }
   }
 };
@@ -302,6 +311,19 @@ __device__ __forceinline__ frag_t<T> frag_col(const FA_LDS char* tile, int base,
       out[s] = *(const FA_LDS float*)(p + (s >= 4 ? 2 * L::S4 : 0) + (s & 3) * L::S1);
     return out;
   }
+}
+
+// Row fragment in frag_col's k-slot order: for lane l (h = l/32), row
+// rb + l%32 of the tile, elements 16 ks + 4h + 0..3 then 16 ks + 8 + 4h + 0..3
+// (bf16).  It pairs with a frag_col operand over the same 16 k values.
+// `base` = Layout::off(lane % 32) + 8 * (lane / 32).
+template <int D, bool DUAL = false>
+__device__ __forceinline__ bf16x8 frag_row_perm(const FA_LDS char* tile, int base, int rb, int ks) {
+  using L = Layout<bf16, D, DUAL>;
+  const FA_LDS char* p = tile + base + L::off(rb) + ks * 32;
+  const bf16x4 x = *(const FA_LDS bf16x4*)p;
+  const bf16x4 y = *(const FA_LDS bf16x4*)(p + 16);
+  return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
 
 // 8 consecutive elements of a row of a (N, D) global matrix at column 8 * c8.

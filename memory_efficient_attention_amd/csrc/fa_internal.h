@@ -136,6 +136,26 @@ struct PreParams {
   long long rows;
 };
 
+// Fused linear cross-entropy (bf16 H (N, D), W (V, D)).
+struct LceParams {
+  const void* h;
+  const void* w;
+  const int32_t* targets;
+  float* nll;            // forward outputs (N,)
+  float* lse;
+  float* tlogit;
+  float* part;           // forward workspace: (ceil(V / 256), N) float2 partial (max, sum)
+  const float* lse_in;   // backward inputs (N,)
+  const float* dnll;
+  void* dz;              // backward workspace: (N, VC) bf16
+  float* dh32;           // backward workspace: (N, D) fp32 accumulator (several chunks)
+  void* dh;              // (N, D) bf16
+  void* dw;              // (V, D) bf16 or null
+  int N, V, D;
+};
+hipError_t launch_lce_fwd(const LceParams& p, hipStream_t s);
+hipError_t launch_lce_bwd(const LceParams& p, int vc, hipStream_t s, void* const* events);
+
 // Launchers (defined next to their kernels).  dtype: 0 bf16, 1 fp32; nw:
 // waves per workgroup, WAVES_DENSE or WAVES_PACKED.
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s);

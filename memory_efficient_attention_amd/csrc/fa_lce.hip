@@ -1,0 +1,372 @@
+// Fused linear cross-entropy: the loss layer of a language model without the
+// (N, V) logits tensor.
+//
+// What is computed follows the mlx-train-perf README, section "The fused
+// cross-entropy loss": for hidden states H (N, D), a dense head W (V, D) and
+// targets t, the forward regenerates the logits Z = H W^T tile by tile and
+// returns three N-length arrays, the per-token NLL, log-sum-exp and target
+// logit; the backward recomputes the tiles it needs instead of reading a
+// stored matrix (README, section "Implementations": the backward the kernel
+// forward pairs with processes the vocabulary in fixed tiles).  With upstream
+// per-token gradients g, dZ = g (softmax(Z) - onehot(t)), dH = dZ W and
+// dW = dZ^T H.
+//
+// All products run on one MFMA GEMM core: a workgroup of 8 waves computes a
+// 256 x 256 tile C = A B (C rows "M", columns "N") with the contraction
+// streamed through LDS in K-slices of 32, each wave a 64 x 128 block (2 x 4
+// MFMA tiles of 32 x 32).  Accumulators use the MFMA layout with lane = N
+// column, so per-column statistics (a token's log-sum-exp) stay in a lane
+// pair.  Operands come from LDS either along rows (a 256 x 32 slice of a
+// row-major matrix whose rows are the M or N index) or transposed (a 32 x 256
+// slice whose rows are the K index), matching k-slot orders pairwise:
+//   forward and dZ:  Z^T  = W   H^T    (A rows of W, B rows of H)
+//   dH:              dH^T = W^T dZ^T   (A transposed W, B rows of dZ, permuted)
+//   dW:              dW^T = H^T dZ     (A transposed H, B transposed dZ)
+// The backward walks the vocabulary in chunks of VC: per chunk, dZ for all
+// tokens is written to a workspace (N x VC bf16), then dH accumulates in an
+// fp32 workspace and dW of the chunk's vocabulary rows is written out.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int TM = 256, TN = 256, TK = 32, NWV = 8;
+constexpr int WM = 64, WN = 128;   // per-wave block: 2 x 4 MFMA tiles
+using LRow = Layout<bf16, TK, false>;     // 256 rows x 32 elements
+using LCol = Layout<bf16, TM, true>;      // 32 rows x 256 elements (transposed reads)
+using StRow = Stager<bf16, TM, TK, NWV, false>;
+using StCol = Stager<bf16, TK, TM, NWV, true>;
+constexpr int ROW_TILE = LRow::bytes(TM);
+constexpr int COL_TILE = LCol::bytes(TK);
+constexpr int TILE_MAX = ROW_TILE > COL_TILE ? ROW_TILE : COL_TILE;
+static_assert(TM == TN, "square C tiles");
+
+// Grouped order of a (mt x nt) grid of C tiles: runs of 8 M tiles sweep all
+// N tiles, so the workgroups resident on one XCD at a time share their
+// operand slices in its L2.  `L` comes through xcd_remap.
+__device__ __forceinline__ void tile_of(int L, int mt, int nt, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int group = L / (GM * nt);
+  const int first = group * GM;
+  const int gm = min(mt - first, GM);
+  const int r = L - group * GM * nt;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+enum Operand { ROWS, COLS, ROWS_PERM };
+
+// The GEMM core.  A (M x K) and B (K x N) are staged per K-slice by
+// stage_a(tile, k0) / stage_b(tile, k0) and read as `OA` / `OB` operands;
+// acc[mb][nb] is the wave's 2 x 4 block of 32 x 32 tiles.
+template <Operand OA, Operand OB, typename SA, typename SB>
+__device__ __forceinline__ void gemm_tile(FA_LDS char* smem, int nk, SA&& stage_a, SB&& stage_b,
+                                          f32x16 (&acc)[2][4], int wave, int lane) {
+  const int wm = wave & 3, wn = wave >> 2;
+  constexpr int LPT = (StRow::NINST > StCol::NINST ? StCol::NINST : StRow::NINST) * 2 / NWV;
+  const int rbase = LRow::row_base(lane);
+  const int pbase = LRow::off(lane & 31) + 8 * (lane >> 5);
+  const int cbase = LCol::col_base(lane);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
+  auto stage = [&](int s, int buf) {
+    stage_a(smem + buf * 2 * TILE_MAX, s * TK);
+    stage_b(smem + buf * 2 * TILE_MAX + TILE_MAX, s * TK);
+  };
+  if (nk > 0) stage(0, 0);
+  for (int s = 0; s < nk; ++s) {
+    const int buf = s & 1;
+    wait_tiles<LPT, 0>(0);
+    __syncthreads();
+    if (s + 1 < nk) stage(s + 1, buf ^ 1);
+    const FA_LDS char* ta = smem + buf * 2 * TILE_MAX;
+    const FA_LDS char* tb = ta + TILE_MAX;
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      bf16x8 a[2], b[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        if constexpr (OA == ROWS) a[mb] = frag_row<bf16, TK, false>(ta, rbase, WM * wm + 32 * mb, ks);
+        else a[mb] = frag_col<bf16, TM>(ta, cbase, 16 * ks, WM * wm + 32 * mb);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if constexpr (OB == ROWS) b[nb] = frag_row<bf16, TK, false>(tb, rbase, WN * wn + 32 * nb, ks);
+        else if constexpr (OB == ROWS_PERM) b[nb] = frag_row_perm<TK>(tb, pbase, WN * wn + 32 * nb, ks);
+        else b[nb] = frag_col<bf16, TN>(tb, cbase, 16 * ks, WN * wn + 32 * nb);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) mma(acc[mb][nb], a[mb], b[nb]);
+    }
+  }
+  __syncthreads();   // the staging buffers may be reused by the epilogue
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- forward
+// One workgroup per (vocabulary tile vt, token tile tt): Z^T for 256 vocabulary
+// rows x 256 tokens over the full hidden size, then per token the tile's max
+// and exp-sum (log2 domain) into part[vt][token], and the target logit where
+// the tile holds it.
+__global__ void __launch_bounds__(NWV * 64, 2) lce_fwd_kernel(const LceParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
+  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int nvt = (p.V + TM - 1) / TM, ntt = (p.N + TN - 1) / TN;
+  int vt, tt;
+  tile_of(xcd_remap(blockIdx.x, nvt * ntt), nvt, ntt, vt, tt);
+  const int v0 = vt * TM, t0 = tt * TN;
+  const int ld = p.D * 2;
+
+  StRow sa, sb;
+  sa.init(wave, lane);
+  sb.init(wave, lane, StRow::NINST);
+  f32x16 acc[2][4];
+  gemm_tile<ROWS, ROWS>(
+      smem, p.D / TK,
+      [&](FA_LDS char* t, int k0) { sa.issue_block(t, p.w, v0, p.V, ld, k0 * 2); },
+      [&](FA_LDS char* t, int k0) { sb.issue_block(t, p.h, t0, p.N, ld, k0 * 2); }, acc, wave, lane);
+
+  const int wm = wave & 3, wn = wave >> 2;
+  float* stat = (float*)smem_raw;   // [4 wm][256 tokens][2]
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int tl = WN * wn + 32 * nb + col;   // token within the tile
+    const int tok = t0 + tl;
+    const int tgt = tok < p.N ? p.targets[tok] : -1;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = v0 + WM * wm + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+        const float z = acc[mb][nb][r];
+        if (v == tgt) p.tlogit[tok] = z;
+        mx = v < p.V ? fmaxf(mx, z) : mx;
+      }
+    mx = fmaxf(mx, other_half(mx));
+    float sum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = v0 + WM * wm + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+        sum += v < p.V ? exp2_fast((acc[mb][nb][r] - mx) * kLog2e) : 0.f;
+      }
+    sum += other_half(sum);
+    if (h == 0) {
+      stat[(wm * TN + tl) * 2] = mx * kLog2e;
+      stat[(wm * TN + tl) * 2 + 1] = sum;
+    }
+  }
+  __syncthreads();
+  if (tid < TN && t0 + tid < p.N) {
+    float m2 = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) m2 = fmaxf(m2, stat[(w * TN + tid) * 2]);
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s += stat[(w * TN + tid) * 2 + 1] * exp2_fast(stat[(w * TN + tid) * 2] - m2);
+    float2* part = (float2*)p.part + (size_t)vt * p.N + t0 + tid;
+    *part = make_float2(m2, s);
+  }
+}
+
+// Per token: combine the vocabulary tiles' (max, sum) into the log-sum-exp,
+// then NLL = LSE - target logit.
+__global__ void __launch_bounds__(256) lce_reduce_kernel(const LceParams p) {
+  const int tok = blockIdx.x * 256 + threadIdx.x;
+  if (tok >= p.N) return;
+  const int nvt = (p.V + TM - 1) / TM;
+  const float2* part = (const float2*)p.part + tok;
+  float m2 = -INFINITY;
+  for (int vt = 0; vt < nvt; ++vt) m2 = fmaxf(m2, part[(size_t)vt * p.N].x);
+  float s = 0.f;
+  for (int vt = 0; vt < nvt; ++vt) {
+    const float2 q = part[(size_t)vt * p.N];
+    s += q.y * exp2_fast(q.x - m2);
+  }
+  const float lse = (m2 + log2_fast(s)) * kLn2;
+  p.lse[tok] = lse;
+  p.nll[tok] = lse - p.tlogit[tok];
+}
+
+// ---------------------------------------------------------------- backward
+// dZ of vocabulary chunk [c0, c0 + VC): one workgroup per (vocabulary tile,
+// token tile) of the chunk, Z^T recomputed as in the forward, then
+// dZ = g (exp(Z - LSE) - [v = t]) stored as bf16 to dz[token][v - c0] (zeros
+// past V, so the following products see none of those columns).
+__global__ void __launch_bounds__(NWV * 64, 2) lce_dz_kernel(const LceParams p, int c0, int vc) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
+  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int nvt = (vc + TM - 1) / TM, ntt = (p.N + TN - 1) / TN;
+  int vt, tt;
+  tile_of(xcd_remap(blockIdx.x, nvt * ntt), nvt, ntt, vt, tt);
+  const int v0 = c0 + vt * TM, t0 = tt * TN;
+  const int ld = p.D * 2;
+
+  StRow sa, sb;
+  sa.init(wave, lane);
+  sb.init(wave, lane, StRow::NINST);
+  f32x16 acc[2][4];
+  gemm_tile<ROWS, ROWS>(
+      smem, p.D / TK,
+      [&](FA_LDS char* t, int k0) { sa.issue_block(t, p.w, v0, p.V, ld, k0 * 2); },
+      [&](FA_LDS char* t, int k0) { sb.issue_block(t, p.h, t0, p.N, ld, k0 * 2); }, acc, wave, lane);
+
+  const int wm = wave & 3, wn = wave >> 2;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int tok = t0 + WN * wn + 32 * nb + col;
+    if (tok >= p.N) continue;
+    const int tgt = p.targets[tok];
+    const float nl2 = -p.lse_in[tok] * kLog2e;
+    const float g = p.dnll[tok];
+    bf16* row = (bf16*)p.dz + (size_t)tok * vc;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = v0 + WM * wm + 32 * mb + 8 * j + 4 * h;   // first of 4 consecutive
+        f32x4 d;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pz = exp2_fast(fmaf(acc[mb][nb][4 * j + i], kLog2e, nl2));
+          d[i] = v + i < p.V ? g * (pz - (v + i == tgt ? 1.f : 0.f)) : 0.f;
+        }
+        if (v - c0 < vc) *(bf16x4*)(row + (v - c0)) = __builtin_convertvector(d, bf16x4);
+      }
+  }
+}
+
+// dH^T (D x N) += W^T dZ^T over the chunk: one workgroup per (hidden tile,
+// token tile).  `mode`: 0 the only chunk (write dh), 1 first (write the fp32
+// accumulator), 2 middle (accumulate), 3 last (accumulate and write dh).
+__global__ void __launch_bounds__(NWV * 64, 2) lce_dh_kernel(const LceParams p, int c0, int vc,
+                                                              int kvalid, int mode) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
+  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int ndt = p.D / TM, ntt = (p.N + TN - 1) / TN;
+  int dt, tt;
+  tile_of(xcd_remap(blockIdx.x, ndt * ntt), ndt, ntt, dt, tt);
+  const int d0 = dt * TM, t0 = tt * TN;
+
+  StCol sa;
+  StRow sb;
+  sa.init(wave, lane);
+  sb.init(wave, lane, StCol::NINST);
+  f32x16 acc[2][4];
+  gemm_tile<COLS, ROWS_PERM>(
+      smem, (kvalid + TK - 1) / TK,
+      // W rows c0 + k0 .. +31 (rows past V read as zeros), hidden columns d0 .. d0 + 255
+      [&](FA_LDS char* t, int k0) { sa.issue_block(t, p.w, c0 + k0, p.V, p.D * 2, d0 * 2); },
+      // dZ rows t0 .. t0 + 255, chunk columns k0 .. k0 + 31
+      [&](FA_LDS char* t, int k0) { sb.issue_block(t, p.dz, t0, p.N, vc * 2, k0 * 2); }, acc, wave, lane);
+
+  const int wm = wave & 3, wn = wave >> 2;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int tok = t0 + WN * wn + 32 * nb + col;
+    if (tok >= p.N) continue;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = d0 + WM * wm + 32 * mb + 8 * j + 4 * h;
+        const size_t e = (size_t)tok * p.D + d;
+        f32x4 x = {acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]};
+        if (mode >= 2) x += *(const f32x4*)(p.dh32 + e);
+        if (mode == 1 || mode == 2) *(f32x4*)(p.dh32 + e) = x;
+        else *(bf16x4*)((bf16*)p.dh + e) = __builtin_convertvector(x, bf16x4);
+      }
+  }
+}
+
+// dW^T (D x VC) = H^T dZ over all tokens for the chunk's vocabulary rows: one
+// workgroup per (hidden tile, vocabulary tile of the chunk).
+__global__ void __launch_bounds__(NWV * 64, 2) lce_dw_kernel(const LceParams p, int c0, int vc) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
+  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int ndt = p.D / TM, nvt = (vc + TN - 1) / TN;
+  int dt, vt;
+  tile_of(xcd_remap(blockIdx.x, ndt * nvt), ndt, nvt, dt, vt);
+  const int d0 = dt * TM, vl0 = vt * TN;   // vl: column of the chunk
+
+  StCol sa, sb;
+  sa.init(wave, lane);
+  sb.init(wave, lane, StCol::NINST);
+  f32x16 acc[2][4];
+  gemm_tile<COLS, COLS>(
+      smem, (p.N + TK - 1) / TK,
+      // H rows k0 .. k0 + 31 (tokens; rows past N read as zeros), hidden columns d0 ..
+      [&](FA_LDS char* t, int k0) { sa.issue_block(t, p.h, k0, p.N, p.D * 2, d0 * 2); },
+      // dZ rows k0 .. k0 + 31, chunk columns vl0 .. vl0 + 255
+      [&](FA_LDS char* t, int k0) { sb.issue_block(t, p.dz, k0, p.N, vc * 2, vl0 * 2); }, acc, wave, lane);
+
+  const int wm = wave & 3, wn = wave >> 2;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int v = c0 + vl0 + WN * wn + 32 * nb + col;
+    if (v >= p.V || v - c0 >= vc) continue;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = d0 + WM * wm + 32 * mb + 8 * j + 4 * h;
+        f32x4 x = {acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]};
+        *(bf16x4*)((bf16*)p.dw + (size_t)v * p.D + d) = __builtin_convertvector(x, bf16x4);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_lce_fwd(const LceParams& p, hipStream_t s) {
+  const int nvt = (p.V + TM - 1) / TM, ntt = (p.N + TN - 1) / TN;
+  hipLaunchKernelGGL(lce_fwd_kernel, dim3((unsigned)(nvt * ntt)), dim3(NWV * 64), 0, s, p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(lce_reduce_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_lce_bwd(const LceParams& p, int vc, hipStream_t s, void* const* events) {
+  const int ntt = (p.N + TN - 1) / TN, ndt = p.D / TM;
+  const int nchunks = (p.V + vc - 1) / vc;
+  for (int c = 0; c < nchunks; ++c) {
+    const int c0 = c * vc;
+    const int kvalid = min(vc, p.V - c0);
+    const int nvt = (vc + TM - 1) / TM;
+    if (events && events[0] && c == 0) (void)hipEventRecord((hipEvent_t)events[0], s);
+    hipLaunchKernelGGL(lce_dz_kernel, dim3((unsigned)(nvt * ntt)), dim3(NWV * 64), 0, s, p, c0, vc);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    const int mode = nchunks == 1 ? 0 : (c == 0 ? 1 : (c + 1 == nchunks ? 3 : 2));
+    hipLaunchKernelGGL(lce_dh_kernel, dim3((unsigned)(ndt * ntt)), dim3(NWV * 64), 0, s, p, c0, vc, kvalid,
+                       mode);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    if (p.dw) {
+      const int nvc = (vc + TN - 1) / TN;
+      hipLaunchKernelGGL(lce_dw_kernel, dim3((unsigned)(ndt * nvc)), dim3(NWV * 64), 0, s, p, c0, vc);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace fa

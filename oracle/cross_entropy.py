@@ -34,7 +34,7 @@ __all__ = ["lce_forward", "lce_backward", "lce_rows"]
 
 def _check(h, w, targets):
     h = np.asarray(h, dtype=np.float64)
-    w = np.asarray(w, dtype=np.float64)
+    w = np.asarray(w)                 # converted to float64 a block of rows at a time
     t = np.asarray(targets, dtype=np.int64)
     if h.ndim != 2 or w.ndim != 2 or h.shape[1] != w.shape[1] or t.shape != (h.shape[0],):
         raise ValueError("expected h (N, D), w (V, D), targets (N,)")
@@ -43,8 +43,16 @@ def _check(h, w, targets):
     return h, w, t
 
 
+def _logits(hr, w, vocab_block=16384):
+    """hr (R, D) float64 times w^T, w converted to float64 in row blocks."""
+    z = np.empty((hr.shape[0], w.shape[0]))
+    for v0 in range(0, w.shape[0], vocab_block):
+        z[:, v0:v0 + vocab_block] = hr @ np.asarray(w[v0:v0 + vocab_block], dtype=np.float64).T
+    return z
+
+
 def _block(h, w, t, rows):
-    z = h[rows] @ w.T
+    z = _logits(h[rows], w)
     m = z.max(axis=1)
     lse = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
     tz = z[np.arange(rows.size), t[rows]]
@@ -69,15 +77,16 @@ def lce_backward(h, w, targets, g, row_block=1024):
     h, w, t = _check(h, w, targets)
     g = np.asarray(g, dtype=np.float64)
     N = h.shape[0]
+    w64 = np.asarray(w, dtype=np.float64)
     dh = np.empty_like(h)
-    dw = np.zeros_like(w)
+    dw = np.zeros_like(w64)
     for r0 in range(0, N, row_block):
         rows = np.arange(r0, min(r0 + row_block, N))
-        z, l, _ = _block(h, w, t, rows)
+        z, l, _ = _block(h, w64, t, rows)
         dz = np.exp(z - l[:, None])
         dz[np.arange(rows.size), t[rows]] -= 1.0
         dz *= g[rows][:, None]
-        dh[rows] = dz @ w
+        dh[rows] = dz @ w64
         dw += dz.T @ h[rows]
     return dh, dw
 
@@ -92,4 +101,7 @@ def lce_rows(h, w, targets, g, rows):
     dz = np.exp(z - l[:, None])
     dz[np.arange(rows.size), t[rows]] -= 1.0
     dz *= g[rows][:, None]
-    return l - z_t, l, z_t, dz @ w
+    dh = np.zeros((rows.size, h.shape[1]))
+    for v0 in range(0, w.shape[0], 16384):
+        dh += dz[:, v0:v0 + 16384] @ np.asarray(w[v0:v0 + 16384], dtype=np.float64)
+    return l - z_t, l, z_t, dh

@@ -42,8 +42,8 @@ def test_header_status_values_match():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
-    assert declared == ["fa_bwd", "fa_bwd_timed", "fa_check_seg", "fa_fwd", "fa_status_string",
-                        "fa_workspace_bytes"]
+    assert declared == ["fa_bwd", "fa_bwd_timed", "fa_check_seg", "fa_fwd", "fa_lce_bwd", "fa_lce_fwd",
+                        "fa_lce_workspace_bytes", "fa_status_string", "fa_workspace_bytes"]
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = sorted(set(re.findall(r" T (fa_\w+)", out)))
     assert exported == declared          # and nothing else leaks out of the library
@@ -163,3 +163,53 @@ def test_status_strings(lib):
         seen.add(txt)
     assert len(seen) == 11
     assert lib.fa_status_string(1234).decode() == "unknown status"
+
+
+# ---------------------------------------------------------------- linear cross-entropy
+
+def _lce_fwd(lib, h=P, w=P, t=P, nll=P, lse=P, tz=P, N=64, V=1000, D=256, dtype=0, ws=P, ws_bytes=1 << 30):
+    lib.fa_lce_fwd.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                                           ctypes.c_void_p]
+    return lib.fa_lce_fwd(h, w, t, nll, lse, tz, N, V, D, dtype, ws, ws_bytes, None)
+
+
+def _lce_bwd(lib, h=P, w=P, t=P, lse=P, g=P, dh=P, dw=P, N=64, V=1000, D=256, dtype=0, ws=P,
+             ws_bytes=1 << 30):
+    lib.fa_lce_bwd.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                                           ctypes.c_void_p]
+    return lib.fa_lce_bwd(h, w, t, lse, g, dh, dw, N, V, D, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=None), FA_ERR_NULL), (dict(t=None), FA_ERR_NULL), (dict(tz=None), FA_ERR_NULL),
+    (dict(N=0), FA_ERR_SHAPE), (dict(V=0), FA_ERR_SHAPE), (dict(D=0), FA_ERR_SHAPE),
+    (dict(D=320), FA_ERR_SHAPE), (dict(V=1 << 20, D=1024), FA_ERR_SHAPE),
+    (dict(N=1 << 17), FA_ERR_SHAPE),
+    (dict(dtype=1), FA_ERR_DTYPE), (dict(dtype=5), FA_ERR_DTYPE),
+    (dict(h=P + 8), FA_ERR_ALIGN), (dict(nll=P + 2), FA_ERR_ALIGN),
+    (dict(ws=None), FA_ERR_WORKSPACE), (dict(ws_bytes=64), FA_ERR_WORKSPACE), (dict(ws=P + 128), FA_ERR_ALIGN),
+])
+def test_lce_fwd_refusals(lib, kw, status):
+    assert _lce_fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None), FA_ERR_NULL), (dict(dh=None), FA_ERR_NULL), (dict(lse=None), FA_ERR_NULL),
+    (dict(D=100), FA_ERR_SHAPE), (dict(dtype=1), FA_ERR_DTYPE),
+    (dict(dw=P + 8), FA_ERR_ALIGN), (dict(g=P + 1), FA_ERR_ALIGN),
+    (dict(ws=None), FA_ERR_WORKSPACE), (dict(ws_bytes=1024), FA_ERR_WORKSPACE),
+])
+def test_lce_bwd_refusals(lib, kw, status):
+    assert _lce_bwd(lib, **kw) == status
+
+
+def test_lce_workspace_sizes(lib):
+    ws = lib.fa_lce_workspace_bytes
+    ws.argtypes = [ctypes.c_int] * 4
+    ws.restype = ctypes.c_size_t
+    assert ws(8192, 151936, 4096, 0) == 594 * 8192 * 8       # per-tile (max, sum) pairs
+    # one dZ chunk of 8192 vocabulary columns, plus the fp32 dh accumulator when
+    # the vocabulary spans several chunks
+    assert ws(8192, 151936, 4096, 1) == 8192 * 8192 * 2 + 8192 * 4096 * 4
+    assert ws(100, 5000, 256, 1) == 100 * 8192 * 2
+    assert ws(100, 5000, 255, 1) == 0 and ws(0, 5000, 256, 0) == 0

@@ -1,0 +1,103 @@
+"""GPU parity of the fused linear cross-entropy, called through the C ABI,
+against the fp64 oracle.
+
+Bounds: NLL, LSE and target logit max-abs <= 1e-3 (scaled by |x| / 10 above
+10): the logits are fp32 sums of bf16 products, so their error is ~1e-6 of
+|h| |w|, and the log-sum-exp adds a few fp32 ulps; dH and dW relative L2
+<= 2e-2, the attention gradients' bf16 bound (dZ is rounded to bf16 before the
+two products).  Small shapes run the whole oracle, with vocabularies spanning
+one, two and three backward chunks and ragged tails in every dimension; the
+full 8192 x 151936 x 4096 shape checks sampled tokens and an identity.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import down, rel_l2, say
+from oracle import lce_backward, lce_forward, lce_rows
+
+pytestmark = pytest.mark.gpu
+
+ABS = 1e-3
+REL_L2 = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import memory_efficient_attention_amd as fa
+    fa.load_library()
+    yield
+
+
+def _up(x, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    return t.to(dtype) if dtype is not None else t
+
+
+def _run(x, need_dw=True):
+    import torch
+    import memory_efficient_attention_amd as fa
+    h, w = _up(x["h"], torch.bfloat16), _up(x["w"], torch.bfloat16)
+    t, g = _up(x["targets"]), _up(x["dnll"])
+    nll, lse, tz = fa.fa_lce_fwd(h, w, t)
+    dh, dw = fa.fa_lce_bwd(h, w, t, lse, g, need_dw=need_dw)
+    torch.cuda.synchronize()
+    return dict(nll=nll, lse=lse, tz=tz, dh=dh, dw=dw)
+
+
+def _check_abs(name, got, ref):
+    err = np.abs(got - ref)
+    bound = ABS * np.maximum(1.0, np.abs(ref) / 10.0)
+    assert not (err > bound).any(), f"{name}: worst err {err.max():.3e}"
+    return float(err.max())
+
+
+@pytest.mark.parametrize("N,V,D", [(300, 1000, 256), (1, 7, 256), (64, 300, 512), (257, 8200, 256),
+                                   (513, 20000, 256)])
+def test_lce_small_shapes(N, V, D):
+    say(f"lce N{N} V{V} D{D}")
+    x = workloads.make_lce_inputs(N, V, D, seed=N + V + D, targets_edge=True)
+    out = _run(x)
+    nll, lse, tz = lce_forward(x["h"], x["w"], x["targets"])
+    dh, dw = lce_backward(x["h"], x["w"], x["targets"], x["dnll"])
+    _check_abs("nll", down(out["nll"]), nll)
+    _check_abs("lse", down(out["lse"]), lse)
+    _check_abs("tlogit", down(out["tz"]), tz)
+    for name, g, r in (("dh", down(out["dh"]), dh), ("dw", down(out["dw"]), dw)):
+        e = rel_l2(g, r)
+        say(f"  {name} rel-L2 {e:.2e}")
+        assert e <= REL_L2, f"{name}: relative L2 {e:.3e}"
+
+
+def test_lce_frozen_head_skips_dw():
+    x = workloads.make_lce_inputs(40, 500, 256, seed=9)
+    a = _run(x, need_dw=False)
+    b = _run(x)
+    assert a["dw"] is None
+    assert bool((a["dh"] == b["dh"]).all())
+
+
+def test_lce_full_size():
+    """The pages' loss-layer shape: N = 8192, V = 151936, D = 4096."""
+    c = workloads.LCE_WORKLOAD
+    say(f"lce workload {c['name']}: {c['note']}")
+    x = workloads.make_lce_inputs(c["N"], c["V"], c["D"], c["seed"], targets_edge=True)
+    out = _run(x)
+    rows = np.array([0, 1, 4095, 8191] + list(np.random.default_rng(8).integers(0, c["N"], 4)))
+    say(f"  oracle rows {rows.tolist()}")
+    r_nll, r_lse, r_tz, r_dh = lce_rows(x["h"], x["w"], x["targets"], x["dnll"], rows)
+    _check_abs("nll", down(out["nll"])[rows], r_nll)
+    _check_abs("lse", down(out["lse"])[rows], r_lse)
+    _check_abs("tlogit", down(out["tz"])[rows], r_tz)
+    e = rel_l2(down(out["dh"])[rows], r_dh)
+    say(f"  dh rows rel-L2 {e:.2e}")
+    assert e <= REL_L2
+    # every row of dZ sums to zero, so sum over the vocabulary of dW vanishes
+    # (bounded by the rounding of dZ to bf16 against the sum of magnitudes)
+    dw = out["dw"].double()
+    s, m = dw.sum(dim=0).abs(), dw.abs().sum(dim=0)
+    assert bool((s <= 1e-2 * m + 1e-6).all()), f"sum dW: worst {(s / (m + 1e-30)).max().item():.3e}"

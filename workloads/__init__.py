@@ -38,9 +38,20 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """float32 values rounded to the nearest bf16 value, returned as float32."""
-    b = bf16_bits(x).astype(np.uint32) << 16
-    return b.view(np.float32)
+    """float32 values rounded to the nearest bf16 value, returned as float32.
+
+    The same rounding as bf16_bits, done in 32-bit integers: adding at most
+    0x8000 cannot wrap for any finite value or infinity (only NaN patterns sit
+    that close to 2^32), so no 64-bit temporaries are needed."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = u + np.uint32(0x7FFF)
+    r += (u >> np.uint32(16)) & np.uint32(1)
+    r &= np.uint32(0xFFFF0000)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = (bf16_bits(x[nan]).astype(np.uint32) << 16)
+    return r.view(np.float32)
 
 
 def seg_from_lengths(rows: list[list[int]], N: int) -> np.ndarray:
@@ -218,6 +229,28 @@ WORKLOADS = {
     "causal_8k_d96": Workload("causal_8k_d96", 1, 32, 8192, 96, "bf16", "none", 7,
                               note="B1 H32 N8192 D96 bf16, causal"),
 }
+
+
+def make_lce_inputs(N: int, V: int, D: int, seed: int, targets_edge: bool = False) -> dict[str, np.ndarray]:
+    """Inputs of the linear cross-entropy loss layer: hidden states h (N, D)
+    iid N(0, 1), a head w (V, D) iid N(0, 1/D) (so that logits are O(1), as
+    after a normalised final layer), both bf16-rounded, targets (N,) int32
+    uniform over [0, V), and per-token upstream gradients dnll (N,) = 1/N (a
+    mean).  With targets_edge the first and last targets are 0 and V - 1."""
+    rng = np.random.default_rng([seed, 3])
+    h = bf16_round(rng.standard_normal((N, D), dtype=np.float32))
+    w = np.empty((V, D), dtype=np.float32)
+    for r0 in range(0, V, 8192):                  # bounded temporaries at V = 151936
+        r1 = min(r0 + 8192, V)
+        w[r0:r1] = bf16_round(rng.standard_normal((r1 - r0, D), dtype=np.float32) / np.float32(np.sqrt(D)))
+    t = rng.integers(0, V, N).astype(np.int32)
+    if targets_edge and N >= 2:
+        t[0], t[-1] = 0, V - 1
+    return {"h": h, "w": w, "targets": t, "dnll": np.full(N, 1.0 / N, dtype=np.float32)}
+
+
+LCE_WORKLOAD = dict(name="lce_8k", N=8192, V=151936, D=4096, seed=8,
+                    note="N8192 V151936 D4096 bf16 fused linear cross-entropy")
 
 
 def get(name: str) -> Workload:
