@@ -179,7 +179,10 @@ const char* fa_status_string(fa_status status);
 size_t fa_lce_workspace_bytes(int N, int V, int D, int for_bwd);
 
 /* Forward: nll[i] = lse[i] - tlogit[i], lse[i] = ln sum_v exp(Z[i][v]),
- * tlogit[i] = Z[i][targets[i]]; all (N,) fp32, written. */
+ * tlogit[i] = Z[i][targets[i]]; all (N,) fp32, written.  Targets are not
+ * validated on the host (they live on the device): a target outside [0, V)
+ * gives NaN tlogit and nll for that token, and in fa_lce_bwd a gradient row
+ * without the one-hot term.  No access goes out of bounds either way. */
 fa_status fa_lce_fwd(const void* h, const void* w, const int32_t* targets,
                      float* nll, float* lse, float* tlogit,
                      int N, int V, int D, fa_dtype dtype,

@@ -197,7 +197,11 @@ __global__ void __launch_bounds__(256) lce_reduce_kernel(const LceParams p) {
   }
   const float lse = (m2 + log2_fast(s)) * kLn2;
   p.lse[tok] = lse;
-  p.nll[tok] = lse - p.tlogit[tok];
+  // a target outside [0, V) was never captured: report NaN, not stale memory
+  const int tgt = p.targets[tok];
+  const float tz = (tgt >= 0 && tgt < p.V) ? p.tlogit[tok] : __builtin_nanf("");
+  p.tlogit[tok] = tz;
+  p.nll[tok] = lse - tz;
 }
 
 // ---------------------------------------------------------------- backward
@@ -205,13 +209,13 @@ __global__ void __launch_bounds__(256) lce_reduce_kernel(const LceParams p) {
 // token tile) of the chunk, Z^T recomputed as in the forward, then
 // dZ = g (exp(Z - LSE) - [v = t]) stored as bf16 to dz[token][v - c0] (zeros
 // past V, so the following products see none of those columns).
-__global__ void __launch_bounds__(NWV * 64, 2) lce_dz_kernel(const LceParams p, int c0, int vc) {
+__global__ void __launch_bounds__(NWV * 64, 2) lce_dz_kernel(const LceParams p, int c0, int vc, int kvalid) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
-  const int nvt = (vc + TM - 1) / TM, ntt = (p.N + TN - 1) / TN;
+  const int nvt = (kvalid + TM - 1) / TM, ntt = (p.N + TN - 1) / TN;
   int vt, tt;
   tile_of(xcd_remap(blockIdx.x, nvt * ntt), nvt, ntt, vt, tt);
   const int v0 = c0 + vt * TM, t0 = tt * TN;
@@ -299,13 +303,13 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_dh_kernel(const LceParams p, 
 
 // dW^T (D x VC) = H^T dZ over all tokens for the chunk's vocabulary rows: one
 // workgroup per (hidden tile, vocabulary tile of the chunk).
-__global__ void __launch_bounds__(NWV * 64, 2) lce_dw_kernel(const LceParams p, int c0, int vc) {
+__global__ void __launch_bounds__(NWV * 64, 2) lce_dw_kernel(const LceParams p, int c0, int vc, int kvalid) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
-  const int ndt = p.D / TM, nvt = (vc + TN - 1) / TN;
+  const int ndt = p.D / TM, nvt = (kvalid + TN - 1) / TN;
   int dt, vt;
   tile_of(xcd_remap(blockIdx.x, ndt * nvt), ndt, nvt, dt, vt);
   const int d0 = dt * TM, vl0 = vt * TN;   // vl: column of the chunk
@@ -351,18 +355,20 @@ hipError_t launch_lce_bwd(const LceParams& p, int vc, hipStream_t s, void* const
   const int nchunks = (p.V + vc - 1) / vc;
   for (int c = 0; c < nchunks; ++c) {
     const int c0 = c * vc;
+    // the last chunk may be partial: only the 256-column tiles holding valid
+    // vocabulary rows are computed (dZ columns past V inside such a tile are
+    // written as zeros, and dh reads no further than that tile)
     const int kvalid = min(vc, p.V - c0);
-    const int nvt = (vc + TM - 1) / TM;
+    const int nvt = (kvalid + TM - 1) / TM;
     if (events && events[0] && c == 0) (void)hipEventRecord((hipEvent_t)events[0], s);
-    hipLaunchKernelGGL(lce_dz_kernel, dim3((unsigned)(nvt * ntt)), dim3(NWV * 64), 0, s, p, c0, vc);
+    hipLaunchKernelGGL(lce_dz_kernel, dim3((unsigned)(nvt * ntt)), dim3(NWV * 64), 0, s, p, c0, vc, kvalid);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     const int mode = nchunks == 1 ? 0 : (c == 0 ? 1 : (c + 1 == nchunks ? 3 : 2));
     hipLaunchKernelGGL(lce_dh_kernel, dim3((unsigned)(ndt * ntt)), dim3(NWV * 64), 0, s, p, c0, vc, kvalid,
                        mode);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (p.dw) {
-      const int nvc = (vc + TN - 1) / TN;
-      hipLaunchKernelGGL(lce_dw_kernel, dim3((unsigned)(ndt * nvc)), dim3(NWV * 64), 0, s, p, c0, vc);
+      hipLaunchKernelGGL(lce_dw_kernel, dim3((unsigned)(ndt * nvt)), dim3(NWV * 64), 0, s, p, c0, vc, kvalid);
       if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
   }
