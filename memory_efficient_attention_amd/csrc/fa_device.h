@@ -313,19 +313,6 @@ __device__ __forceinline__ frag_t<T> frag_col(const FA_LDS char* tile, int base,
   }
 }
 
-// Row fragment in frag_col's k-slot order: for lane l (h = l/32), row
-// rb + l%32 of the tile, elements 16 ks + 4h + 0..3 then 16 ks + 8 + 4h + 0..3
-// (bf16).  It pairs with a frag_col operand over the same 16 k values.
-// `base` = Layout::off(lane % 32) + 8 * (lane / 32).
-template <int D, bool DUAL = false>
-__device__ __forceinline__ bf16x8 frag_row_perm(const FA_LDS char* tile, int base, int rb, int ks) {
-  using L = Layout<bf16, D, DUAL>;
-  const FA_LDS char* p = tile + base + L::off(rb) + ks * 32;
-  const bf16x4 x = *(const FA_LDS bf16x4*)p;
-  const bf16x4 y = *(const FA_LDS bf16x4*)(p + 16);
-  return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-}
-
 // 8 consecutive elements of a row of a (N, D) global matrix at column 8 * c8.
 template <typename T, int D>
 __device__ __forceinline__ frag_t<T> gfrag_row(const T* g, int row, int c8) {

@@ -13,15 +13,20 @@
 //
 // All products run on one MFMA GEMM core: a workgroup of 8 waves computes a
 // 256 x 256 tile C = A B (C rows "M", columns "N") with the contraction
-// streamed through LDS in K-slices of 32, each wave a 64 x 128 block (2 x 4
-// MFMA tiles of 32 x 32).  Accumulators use the MFMA layout with lane = N
+// streamed through LDS in K-slices of TK = 64, each wave a 64 x 128 block
+// (2 x 4 MFMA tiles of 32 x 32).  Accumulators use the MFMA layout with lane = N
 // column, so per-column statistics (a token's log-sum-exp) stay in a lane
-// pair.  Operands come from LDS either along rows (a 256 x 32 slice of a
-// row-major matrix whose rows are the M or N index) or transposed (a 32 x 256
+// pair.  Operands come from LDS either along rows (a 256 x TK slice of a
+// row-major matrix whose rows are the M or N index) or transposed (a TK x 256
 // slice whose rows are the K index), matching k-slot orders pairwise:
 //   forward and dZ:  Z^T  = W   H^T    (A rows of W, B rows of H)
-//   dH:              dH^T = W^T dZ^T   (A transposed W, B rows of dZ, permuted)
+//   dH:              dH^T = W^T dZ^T   (A transposed W, B rows of dZ)
 //   dW:              dW^T = H^T dZ     (A transposed H, B transposed dZ)
+// The transposed read delivers a lane's 8 k-slots of a 16-wide step in the
+// order {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32).  dZ is an intermediate of
+// our own, so it is stored with the two middle 4-column groups of every 16
+// swapped (dz_pos): a plain 16-byte row read of it then yields exactly that
+// order, and dH pairs it with transposed W without a split read.
 // The backward walks the vocabulary in chunks of VC: per chunk, dZ for all
 // tokens is written to a workspace (N x VC bf16), then dH accumulates in an
 // fp32 workspace and dW of the chunk's vocabulary rows is written out.
@@ -32,10 +37,32 @@ namespace fa {
 
 namespace {
 
-constexpr int TM = 256, TN = 256, TK = 32, NWV = 8;
-constexpr int WM = 64, WN = 128;   // per-wave block: 2 x 4 MFMA tiles
-using LRow = Layout<bf16, TK, false>;     // 256 rows x 32 elements
-using LCol = Layout<bf16, TM, true>;      // 32 rows x 256 elements (transposed reads)
+// Per-wave block WM x WN (MB x NB MFMA tiles of 32 x 32).  64 x 128 runs 8
+// waves at 2 per SIMD; 128 x 128 runs 4 waves at 1 per SIMD, with twice the
+// registers and 2/3 of the LDS reads per MFMA.
+#ifndef FA_LCE_WAVE_M
+#define FA_LCE_WAVE_M 64
+#endif
+#ifndef FA_LCE_STAGES
+#define FA_LCE_STAGES 2
+#endif
+#ifndef FA_LCE_TK
+#define FA_LCE_TK 64
+#endif
+constexpr int TM = 256, TN = 256, TK = FA_LCE_TK;   // contraction slice per stage
+constexpr int WM = FA_LCE_WAVE_M, WN = 128;
+constexpr int MB = WM / 32, NB = WN / 32;
+constexpr int WAVES_M = TM / WM, WAVES_N = TN / WN, NWV = WAVES_M * WAVES_N;
+constexpr int WPE = NWV >= 8 ? 2 : 1;          // waves per SIMD the registers allow
+constexpr int STAGES = FA_LCE_STAGES;
+static_assert(WM == 64 || WM == 128, "per-wave block");
+static_assert(STAGES >= 2 && STAGES <= 4, "stage ring");
+static_assert(TK == 32 || TK == 64, "contraction slice");
+#ifndef FA_LCE_FENCE
+#define FA_LCE_FENCE 1
+#endif
+using LRow = Layout<bf16, TK, false>;     // 256 rows x TK elements
+using LCol = Layout<bf16, TM, true>;      // TK rows x 256 elements (transposed reads)
 using StRow = Stager<bf16, TM, TK, NWV, false>;
 using StCol = Stager<bf16, TK, TM, NWV, true>;
 constexpr int ROW_TILE = LRow::bytes(TM);
@@ -56,55 +83,92 @@ __device__ __forceinline__ void tile_of(int L, int mt, int nt, int& tm, int& tn)
   tn = r / gm;
 }
 
-enum Operand { ROWS, COLS, ROWS_PERM };
+enum Operand { ROWS, COLS };
+
+// Storage position of dZ column j within its chunk: bits 2 and 3 swapped
+// (an involution, so it also maps a stored position back to its column).
+__device__ __forceinline__ int dz_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
 
 // The GEMM core.  A (M x K) and B (K x N) are staged per K-slice by
 // stage_a(tile, k0) / stage_b(tile, k0) and read as `OA` / `OB` operands;
-// acc[mb][nb] is the wave's 2 x 4 block of 32 x 32 tiles.
+// acc[mb][nb] is the wave's MB x NB block of 32 x 32 tiles.  The ring holds
+// STAGES K-slices; slice s + STAGES - 1 is issued once slice s - 1's buffer
+// is free.  Every slice ends at a workgroup barrier, where both waves of a
+// SIMD stop together; so the MFMAs of each slice's last 16-wide step are
+// issued only after the next barrier, where they keep the matrix unit busy
+// while the new slice's first fragments come from LDS.  The order of the
+// MFMAs on each accumulator is unchanged.
 template <Operand OA, Operand OB, typename SA, typename SB>
 __device__ __forceinline__ void gemm_tile(FA_LDS char* smem, int nk, SA&& stage_a, SB&& stage_b,
-                                          f32x16 (&acc)[2][4], int wave, int lane) {
-  const int wm = wave & 3, wn = wave >> 2;
+                                          f32x16 (&acc)[MB][NB], int wave, int lane) {
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  // load instructions per wave per slice, at least (both tiles' stagers deal
+  // round-robin as one set)
   constexpr int LPT = (StRow::NINST > StCol::NINST ? StCol::NINST : StRow::NINST) * 2 / NWV;
+  constexpr int KS = TK / 16;
   const int rbase = LRow::row_base(lane);
-  const int pbase = LRow::off(lane & 31) + 8 * (lane >> 5);
   const int cbase = LCol::col_base(lane);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
   auto stage = [&](int s, int buf) {
     stage_a(smem + buf * 2 * TILE_MAX, s * TK);
     stage_b(smem + buf * 2 * TILE_MAX + TILE_MAX, s * TK);
   };
-  if (nk > 0) stage(0, 0);
+  auto read = [&](const FA_LDS char* ta, const FA_LDS char* tb, int ks, bf16x8 (&a)[MB], bf16x8 (&b)[NB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (OA == ROWS) a[mb] = frag_row<bf16, TK, false>(ta, rbase, WM * wm + 32 * mb, ks);
+      else a[mb] = frag_col<bf16, TM>(ta, cbase, 16 * ks, WM * wm + 32 * mb);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (OB == ROWS) b[nb] = frag_row<bf16, TK, false>(tb, rbase, WN * wn + 32 * nb, ks);
+      else b[nb] = frag_col<bf16, TN>(tb, cbase, 16 * ks, WN * wn + 32 * nb);
+    }
+  };
+  auto mmas = [&](const bf16x8 (&a)[MB], const bf16x8 (&b)[NB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) mma(acc[mb][nb], a[mb], b[nb]);
+  };
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) stage(s, s);
+  bf16x8 pa[MB], pb[NB];   // the previous slice's last step, not yet multiplied
+  int buf = 0;
   for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    wait_tiles<LPT, 0>(0);
+    // slices s + 1 .. s + STAGES - 2 may stay in flight
+    wait_tiles<LPT, STAGES - 2>(min(nk - 1 - s, STAGES - 2));
     __syncthreads();
-    if (s + 1 < nk) stage(s + 1, buf ^ 1);
+    if (s + STAGES - 1 < nk) stage(s + STAGES - 1, buf == 0 ? STAGES - 1 : buf - 1);
     const FA_LDS char* ta = smem + buf * 2 * TILE_MAX;
     const FA_LDS char* tb = ta + TILE_MAX;
+    buf = buf + 1 == STAGES ? 0 : buf + 1;
+    bf16x8 a[MB], b[NB];
+    read(ta, tb, 0, a, b);
+    // keep the reads ahead of the deferred MFMAs (the scheduler would
+    // otherwise hoist the MFMAs, which then block the reads' issue)
+    if (FA_LCE_FENCE) __builtin_amdgcn_sched_barrier(0);
+    if (s > 0) mmas(pa, pb);
 #pragma unroll
-    for (int ks = 0; ks < TK / 16; ++ks) {
-      bf16x8 a[2], b[4];
+    for (int ks = 1; ks < KS; ++ks) {
+      bf16x8 a2[MB], b2[NB];
+      read(ta, tb, ks, a2, b2);
+      mmas(a, b);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        if constexpr (OA == ROWS) a[mb] = frag_row<bf16, TK, false>(ta, rbase, WM * wm + 32 * mb, ks);
-        else a[mb] = frag_col<bf16, TM>(ta, cbase, 16 * ks, WM * wm + 32 * mb);
-      }
+      for (int mb = 0; mb < MB; ++mb) a[mb] = a2[mb];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        if constexpr (OB == ROWS) b[nb] = frag_row<bf16, TK, false>(tb, rbase, WN * wn + 32 * nb, ks);
-        else if constexpr (OB == ROWS_PERM) b[nb] = frag_row_perm<TK>(tb, pbase, WN * wn + 32 * nb, ks);
-        else b[nb] = frag_col<bf16, TN>(tb, cbase, 16 * ks, WN * wn + 32 * nb);
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) mma(acc[mb][nb], a[mb], b[nb]);
+      for (int nb = 0; nb < NB; ++nb) b[nb] = b2[nb];
     }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) pa[mb] = a[mb];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) pb[nb] = b[nb];
   }
+  if (nk > 0) mmas(pa, pb);
   __syncthreads();   // the staging buffers may be reused by the epilogue
 }
 
@@ -115,8 +179,8 @@ __device__ __forceinline__ void gemm_tile(FA_LDS char* smem, int nk, SA&& stage_
 // rows x 256 tokens over the full hidden size, then per token the tile's max
 // and exp-sum (log2 domain) into part[vt][token], and the target logit where
 // the tile holds it.
-__global__ void __launch_bounds__(NWV * 64, 2) lce_fwd_kernel(const LceParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
+__global__ void __launch_bounds__(NWV * 64, WPE) lce_fwd_kernel(const LceParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGES * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -130,22 +194,22 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_fwd_kernel(const LceParams p)
   StRow sa, sb;
   sa.init(wave, lane);
   sb.init(wave, lane, StRow::NINST);
-  f32x16 acc[2][4];
+  f32x16 acc[MB][NB];
   gemm_tile<ROWS, ROWS>(
       smem, p.D / TK,
       [&](FA_LDS char* t, int k0) { sa.issue_block(t, p.w, v0, p.V, ld, k0 * 2); },
       [&](FA_LDS char* t, int k0) { sb.issue_block(t, p.h, t0, p.N, ld, k0 * 2); }, acc, wave, lane);
 
-  const int wm = wave & 3, wn = wave >> 2;
-  float* stat = (float*)smem_raw;   // [4 wm][256 tokens][2]
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  float* stat = (float*)smem_raw;   // [WAVES_M][256 tokens][2]
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int tl = WN * wn + 32 * nb + col;   // token within the tile
     const int tok = t0 + tl;
     const int tgt = tok < p.N ? p.targets[tok] : -1;
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = v0 + WM * wm + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -156,7 +220,7 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_fwd_kernel(const LceParams p)
     mx = fmaxf(mx, other_half(mx));
     float sum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int v = v0 + WM * wm + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -172,30 +236,46 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_fwd_kernel(const LceParams p)
   if (tid < TN && t0 + tid < p.N) {
     float m2 = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) m2 = fmaxf(m2, stat[(w * TN + tid) * 2]);
+    for (int w = 0; w < WAVES_M; ++w) m2 = fmaxf(m2, stat[(w * TN + tid) * 2]);
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) s += stat[(w * TN + tid) * 2 + 1] * exp2_fast(stat[(w * TN + tid) * 2] - m2);
+    for (int w = 0; w < WAVES_M; ++w) s += stat[(w * TN + tid) * 2 + 1] * exp2_fast(stat[(w * TN + tid) * 2] - m2);
     float2* part = (float2*)p.part + (size_t)vt * p.N + t0 + tid;
     *part = make_float2(m2, s);
   }
 }
 
 // Per token: combine the vocabulary tiles' (max, sum) into the log-sum-exp,
-// then NLL = LSE - target logit.
-__global__ void __launch_bounds__(256) lce_reduce_kernel(const LceParams p) {
-  const int tok = blockIdx.x * 256 + threadIdx.x;
-  if (tok >= p.N) return;
+// then NLL = LSE - target logit.  A workgroup takes 64 tokens (one per lane);
+// its 8 waves split the vocabulary tiles round-robin, each folding its share
+// online, and wave 0 folds the 8 results.
+constexpr int RED_TOK = 64, RED_WAVES = 8;
+__global__ void __launch_bounds__(RED_WAVES * 64) lce_reduce_kernel(const LceParams p) {
+  __shared__ float2 stat[RED_WAVES][RED_TOK];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok = blockIdx.x * RED_TOK + lane;
   const int nvt = (p.V + TM - 1) / TM;
-  const float2* part = (const float2*)p.part + tok;
-  float m2 = -INFINITY;
-  for (int vt = 0; vt < nvt; ++vt) m2 = fmaxf(m2, part[(size_t)vt * p.N].x);
-  float s = 0.f;
-  for (int vt = 0; vt < nvt; ++vt) {
-    const float2 q = part[(size_t)vt * p.N];
-    s += q.y * exp2_fast(q.x - m2);
+  float m = -INFINITY, s = 0.f;
+  if (tok < p.N) {
+    const float2* part = (const float2*)p.part + tok;
+    for (int vt = wave; vt < nvt; vt += RED_WAVES) {
+      const float2 q = part[(size_t)vt * p.N];
+      const float mn = fmaxf(m, q.x);
+      s = s * exp2_fast(m - mn) + q.y * exp2_fast(q.x - mn);
+      m = mn;
+    }
   }
-  const float lse = (m2 + log2_fast(s)) * kLn2;
+  stat[wave][lane] = make_float2(m, s);
+  __syncthreads();
+  if (wave != 0 || tok >= p.N) return;
+  float m2 = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < RED_WAVES; ++w) m2 = fmaxf(m2, stat[w][lane].x);
+  float s2 = 0.f;
+#pragma unroll
+  for (int w = 0; w < RED_WAVES; ++w) s2 += stat[w][lane].y * exp2_fast(stat[w][lane].x - m2);
+  const float lse = (m2 + log2_fast(s2)) * kLn2;
   p.lse[tok] = lse;
   // a target outside [0, V) was never captured: report NaN, not stale memory
   const int tgt = p.targets[tok];
@@ -207,10 +287,10 @@ __global__ void __launch_bounds__(256) lce_reduce_kernel(const LceParams p) {
 // ---------------------------------------------------------------- backward
 // dZ of vocabulary chunk [c0, c0 + VC): one workgroup per (vocabulary tile,
 // token tile) of the chunk, Z^T recomputed as in the forward, then
-// dZ = g (exp(Z - LSE) - [v = t]) stored as bf16 to dz[token][v - c0] (zeros
-// past V, so the following products see none of those columns).
-__global__ void __launch_bounds__(NWV * 64, 2) lce_dz_kernel(const LceParams p, int c0, int vc, int kvalid) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
+// dZ = g (exp(Z - LSE) - [v = t]) stored as bf16 to dz[token][dz_pos(v - c0)]
+// (zeros past V, so the following products see none of those columns).
+__global__ void __launch_bounds__(NWV * 64, WPE) lce_dz_kernel(const LceParams p, int c0, int vc, int kvalid) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGES * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -224,15 +304,15 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_dz_kernel(const LceParams p, 
   StRow sa, sb;
   sa.init(wave, lane);
   sb.init(wave, lane, StRow::NINST);
-  f32x16 acc[2][4];
+  f32x16 acc[MB][NB];
   gemm_tile<ROWS, ROWS>(
       smem, p.D / TK,
       [&](FA_LDS char* t, int k0) { sa.issue_block(t, p.w, v0, p.V, ld, k0 * 2); },
       [&](FA_LDS char* t, int k0) { sb.issue_block(t, p.h, t0, p.N, ld, k0 * 2); }, acc, wave, lane);
 
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int tok = t0 + WN * wn + 32 * nb + col;
     if (tok >= p.N) continue;
     const int tgt = p.targets[tok];
@@ -240,7 +320,7 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_dz_kernel(const LceParams p, 
     const float g = p.dnll[tok];
     bf16* row = (bf16*)p.dz + (size_t)tok * vc;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int v = v0 + WM * wm + 32 * mb + 8 * j + 4 * h;   // first of 4 consecutive
@@ -250,7 +330,8 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_dz_kernel(const LceParams p, 
           const float pz = exp2_fast(fmaf(acc[mb][nb][4 * j + i], kLog2e, nl2));
           d[i] = v + i < p.V ? g * (pz - (v + i == tgt ? 1.f : 0.f)) : 0.f;
         }
-        if (v - c0 < vc) *(bf16x4*)(row + (v - c0)) = __builtin_convertvector(d, bf16x4);
+        // v - c0 is a multiple of 4, and dz_pos keeps 4-aligned runs together
+        if (v - c0 < vc) *(bf16x4*)(row + dz_pos(v - c0)) = __builtin_convertvector(d, bf16x4);
       }
   }
 }
@@ -258,9 +339,9 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_dz_kernel(const LceParams p, 
 // dH^T (D x N) += W^T dZ^T over the chunk: one workgroup per (hidden tile,
 // token tile).  `mode`: 0 the only chunk (write dh), 1 first (write the fp32
 // accumulator), 2 middle (accumulate), 3 last (accumulate and write dh).
-__global__ void __launch_bounds__(NWV * 64, 2) lce_dh_kernel(const LceParams p, int c0, int vc,
+__global__ void __launch_bounds__(NWV * 64, WPE) lce_dh_kernel(const LceParams p, int c0, int vc,
                                                               int kvalid, int mode) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGES * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -274,21 +355,21 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_dh_kernel(const LceParams p, 
   StRow sb;
   sa.init(wave, lane);
   sb.init(wave, lane, StCol::NINST);
-  f32x16 acc[2][4];
-  gemm_tile<COLS, ROWS_PERM>(
+  f32x16 acc[MB][NB];
+  gemm_tile<COLS, ROWS>(
       smem, (kvalid + TK - 1) / TK,
-      // W rows c0 + k0 .. +31 (rows past V read as zeros), hidden columns d0 .. d0 + 255
+      // W rows c0 + k0 .. + TK - 1 (rows past V read as zeros), hidden columns d0 .. d0 + 255
       [&](FA_LDS char* t, int k0) { sa.issue_block(t, p.w, c0 + k0, p.V, p.D * 2, d0 * 2); },
-      // dZ rows t0 .. t0 + 255, chunk columns k0 .. k0 + 31
+      // dZ rows t0 .. t0 + 255, chunk positions k0 .. k0 + TK - 1
       [&](FA_LDS char* t, int k0) { sb.issue_block(t, p.dz, t0, p.N, vc * 2, k0 * 2); }, acc, wave, lane);
 
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int tok = t0 + WN * wn + 32 * nb + col;
     if (tok >= p.N) continue;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = d0 + WM * wm + 32 * mb + 8 * j + 4 * h;
@@ -303,8 +384,8 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_dh_kernel(const LceParams p, 
 
 // dW^T (D x VC) = H^T dZ over all tokens for the chunk's vocabulary rows: one
 // workgroup per (hidden tile, vocabulary tile of the chunk).
-__global__ void __launch_bounds__(NWV * 64, 2) lce_dw_kernel(const LceParams p, int c0, int vc, int kvalid) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_MAX];
+__global__ void __launch_bounds__(NWV * 64, WPE) lce_dw_kernel(const LceParams p, int c0, int vc, int kvalid) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGES * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -317,21 +398,23 @@ __global__ void __launch_bounds__(NWV * 64, 2) lce_dw_kernel(const LceParams p, 
   StCol sa, sb;
   sa.init(wave, lane);
   sb.init(wave, lane, StCol::NINST);
-  f32x16 acc[2][4];
+  f32x16 acc[MB][NB];
   gemm_tile<COLS, COLS>(
       smem, (p.N + TK - 1) / TK,
-      // H rows k0 .. k0 + 31 (tokens; rows past N read as zeros), hidden columns d0 ..
+      // H rows k0 .. k0 + TK - 1 (tokens; rows past N read as zeros), hidden columns d0 ..
       [&](FA_LDS char* t, int k0) { sa.issue_block(t, p.h, k0, p.N, p.D * 2, d0 * 2); },
-      // dZ rows k0 .. k0 + 31, chunk columns vl0 .. vl0 + 255
+      // dZ rows k0 .. k0 + TK - 1, chunk positions vl0 .. vl0 + 255
       [&](FA_LDS char* t, int k0) { sb.issue_block(t, p.dz, k0, p.N, vc * 2, vl0 * 2); }, acc, wave, lane);
 
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int v = c0 + vl0 + WN * wn + 32 * nb + col;
-    if (v >= p.V || v - c0 >= vc) continue;
+  for (int nb = 0; nb < NB; ++nb) {
+    // this lane's output column is stored dZ position pc, i.e. vocabulary row c0 + dz_pos(pc)
+    const int pc = vl0 + WN * wn + 32 * nb + col;
+    const int v = c0 + dz_pos(pc);
+    if (v >= p.V || pc >= vc) continue;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = d0 + WM * wm + 32 * mb + 8 * j + 4 * h;
@@ -346,7 +429,8 @@ hipError_t launch_lce_fwd(const LceParams& p, hipStream_t s) {
   const int nvt = (p.V + TM - 1) / TM, ntt = (p.N + TN - 1) / TN;
   hipLaunchKernelGGL(lce_fwd_kernel, dim3((unsigned)(nvt * ntt)), dim3(NWV * 64), 0, s, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL(lce_reduce_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(lce_reduce_kernel, dim3((unsigned)((p.N + RED_TOK - 1) / RED_TOK)), dim3(RED_WAVES * 64), 0,
+                     s, p);
   return hipGetLastError();
 }
 
