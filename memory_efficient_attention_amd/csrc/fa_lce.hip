@@ -85,6 +85,13 @@ __device__ __forceinline__ void tile_of(int L, int mt, int nt, int& tm, int& tn)
 
 enum Operand { ROWS, COLS };
 
+// Complete this wave's LDS reads.  A barrier does not wait for them, and the
+// LDS unit orders them only against other LDS instructions, not against the
+// direct global->LDS loads another wave issues after the barrier; the GEMM
+// loop carries fragments read from a stage buffer across the barrier that
+// frees that buffer, so it drains them first.
+__device__ __forceinline__ void lds_drain() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Storage position of dZ column j within its chunk: bits 2 and 3 swapped
 // (an involution, so it also maps a stored position back to its column).
 __device__ __forceinline__ int dz_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
@@ -142,6 +149,7 @@ __device__ __forceinline__ void gemm_tile(FA_LDS char* smem, int nk, SA&& stage_
   for (int s = 0; s < nk; ++s) {
     // slices s + 1 .. s + STAGES - 2 may stay in flight
     wait_tiles<LPT, STAGES - 2>(min(nk - 1 - s, STAGES - 2));
+    lds_drain();   // pa / pb were read from the buffer this barrier frees
     __syncthreads();
     if (s + STAGES - 1 < nk) stage(s + STAGES - 1, buf == 0 ? STAGES - 1 : buf - 1);
     const FA_LDS char* ta = smem + buf * 2 * TILE_MAX;
