@@ -249,28 +249,42 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
 // the accumulator columns are keys, rows queries), P and dS in registers,
 // dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T through the transposing
 // LDS read.
-template <typename T, int D, bool CAUSAL, int NW>
+// TEAMS = 2 (grouped-query heads, an even group size G): the workgroup's
+// waves form two teams of NW / 2 that own the same keys; team t walks query
+// heads t G / 2 .. (t + 1) G / 2 - 1 of the group, both teams in step (equal
+// trip counts, shared barriers), and team 1 adds its dK and dV into team 0's
+// through LDS at the end.  That gives grouped heads full-occupancy
+// workgroups of equal halves instead of few long, half-occupied ones.
+template <typename T, int D, bool CAUSAL, int NW, int TEAMS = 1>
 __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const BwdParams p) {
-  constexpr int BNK = NW * 32, BMQ = QRY_TILE;
+  constexpr int KW = NW / TEAMS;   // waves along the keys
+  constexpr int BNK = KW * 32, BMQ = QRY_TILE;
   constexpr int KS = D / 16, DB = D / 32, QB = BMQ / 32;
   using L = Layout<T, D>;
   using St = Stager<T, BMQ, D, NW>;
   constexpr int TILE = L::bytes(BMQ);
   constexpr int VEC = BMQ * 4;
-  constexpr int S = sizeof(T) == 2 ? stages_for(FA_DKV_STAGES, 2 * TILE + 3 * VEC, NW) : 2;
-  static_assert(S >= 2 && S * (2 * TILE + 3 * VEC) <= LDS_PER_CU, "Q/dO stages must fit in LDS");
-  // Q and dO tiles share one stager's per-lane offsets when one tile's
-  // instructions already reach every wave; otherwise (D = 64, 8 waves) the
-  // dO stager continues the round-robin so that every wave has a load to
-  // count.
+  constexpr int PER_STAGE = TEAMS * (2 * TILE + 2 * VEC) + VEC;
+  constexpr int S = sizeof(T) == 2 ? stages_for(FA_DKV_STAGES, PER_STAGE, NW) : 2;
+  static_assert(S >= 2 && S * PER_STAGE <= LDS_PER_CU, "Q/dO stages must fit in LDS");
+  static_assert(TEAMS == 1 || (TEAMS == 2 && sizeof(T) == 2), "teams: bf16 only");
+  static_assert(TEAMS == 1 || S * PER_STAGE >= KW * 32 * D * 4, "team reduction reuses the ring");
+  // The 2 TEAMS Q and dO tiles of a stage share one stager's per-lane
+  // offsets when one tile's instructions already reach every wave; otherwise
+  // (D < 128, 8 waves) each further tile's stager continues the round-robin
+  // so that every wave has a load to count.
   constexpr bool SHARE = St::NINST >= NW;
-  constexpr int LPT = SHARE ? 2 * (St::NINST / NW) : 2 * St::NINST / NW;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[S * (2 * TILE + 3 * VEC)];
+  constexpr int LPT = SHARE ? 2 * TEAMS * (St::NINST / NW) : 2 * TEAMS * St::NINST / NW;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[S * PER_STAGE];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
-  // layout: Q[S] | dO[S] | nls[S] | delta[S] | seg[S]
+  // layout: Q[S][TEAMS] | dO[S][TEAMS] | nls[S][TEAMS] | delta[S][TEAMS] | seg[S]
+  constexpr int OFF_DO = S * TEAMS * TILE, OFF_NLS = 2 * S * TEAMS * TILE;
+  constexpr int OFF_DLS = OFF_NLS + S * TEAMS * VEC, OFF_SEG = OFF_DLS + S * TEAMS * VEC;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int team = TEAMS == 1 ? 0 : wave / KW;
+  const int kwave = TEAMS == 1 ? wave : wave % KW;
   const int h = lane >> 5, col = lane & 31;
   const int N = p.N;
   const int nkt = p.ntiles;
@@ -294,12 +308,13 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     const int Lw = xcd_remap(blockIdx.x, p.B * Hkv * nkt);
     bg = Lw / nkt;
     const int l = Lw - bg * nkt;
-    // With grouped heads there are few, long workgroups, all resident at
-    // once, so a head's first key tiles (heaviest under causal masking) are
-    // dispatched in ascending and its second half in descending order: the
-    // two workgroups a CU receives pair a heavy tile with a light one.
+    // With grouped heads and one team there are few, long workgroups, all
+    // resident at once, so a head's first key tiles (heaviest under causal
+    // masking) are dispatched in ascending and its second half in descending
+    // order: the two workgroups a CU receives pair a heavy tile with a light
+    // one.  Teams fill a CU with one workgroup; heaviest first then.
     const int half = (nkt + 1) / 2;
-    kt = (G > 1 && l >= half) ? nkt - 1 - (l - half) : l;
+    kt = (TEAMS == 1 && G > 1 && l >= half) ? nkt - 1 - (l - half) : l;
     b = bg / Hkv;
     qt_lo = CAUSAL ? kt * BNK / BMQ : 0;
     qt_hi = (N - 1) / BMQ;
@@ -309,12 +324,14 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   const T* gk = (const T*)p.k + offkv;
   const T* gv = (const T*)p.v + offkv;
   const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
-  // iteration it covers query head bh0 + it / nq, query tile qt_lo + it % nq
+  // iteration it covers query head bh0 + team GT + it / nq, query tile
+  // qt_lo + it % nq (GT = G / TEAMS heads per team)
+  const int GT = G / TEAMS;
   const int nq = qt_hi - qt_lo + 1;
-  const int nit = nq > 0 ? G * nq : 0;
+  const int nit = nq > 0 ? GT * nq : 0;
 
   const int k0 = kt * BNK;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + kwave * 32;
   const int kj = kw0 + col;
   const int kc_ = min(kj, N - 1);
   const int klast = min(kw0 + 31, N - 1);
@@ -336,6 +353,11 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   St stq, stdo;
   stq.init(wave, lane);
   if constexpr (!SHARE) stdo.init(wave, lane, St::NINST);
+  St stq2, stdo2;   // team 1's tiles, continuing the round-robin
+  if constexpr (TEAMS == 2 && !SHARE) {
+    stq2.init(wave, lane, 2 * St::NINST);
+    stdo2.init(wave, lane, 3 * St::NINST);
+  }
   const int rbase = L::row_base(lane);
   const int cbase = L::col_base(lane);
 
@@ -349,12 +371,16 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   auto stage = [&](int it, int buf) {
     const int hj = it / nq;
     const int r0 = (qt_lo + it - hj * nq) * BMQ;
-    const size_t bh = bh0 + hj;
-    stq.issue(smem + buf * TILE, (const T*)p.q + bh * N * D, r0, N);
-    (SHARE ? stq : stdo).issue(smem + (S + buf) * TILE, (const T*)p.dO + bh * N * D, r0, N);
-    stage_vec<BMQ>(smem + 2 * S * TILE + buf * VEC, p.nls + bh * N, r0, N, wave, 0, lane);
-    stage_vec<BMQ>(smem + 2 * S * TILE + (S + buf) * VEC, p.delta + bh * N, r0, N, wave, 1 % NW, lane);
-    if (packed) stage_vec<BMQ>(smem + 2 * S * TILE + (2 * S + buf) * VEC, seg, r0, N, wave, 2 % NW, lane);
+#pragma unroll
+    for (int t = 0; t < TEAMS; ++t) {
+      const size_t bh = bh0 + t * GT + hj;
+      const int slot = buf * TEAMS + t;
+      (SHARE || t == 0 ? stq : stq2).issue(smem + slot * TILE, (const T*)p.q + bh * N * D, r0, N);
+      (SHARE ? stq : (t == 0 ? stdo : stdo2)).issue(smem + OFF_DO + slot * TILE, (const T*)p.dO + bh * N * D, r0, N);
+      stage_vec<BMQ>(smem + OFF_NLS + slot * VEC, p.nls + bh * N, r0, N, wave, (2 * t) % NW, lane);
+      stage_vec<BMQ>(smem + OFF_DLS + slot * VEC, p.delta + bh * N, r0, N, wave, (2 * t + 1) % NW, lane);
+    }
+    if (packed) stage_vec<BMQ>(smem + OFF_SEG + buf * VEC, seg, r0, N, wave, (2 * TEAMS) % NW, lane);
   };
 
   // Ring of S stages, as in the forward.
@@ -376,11 +402,12 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     if (it + S - 1 < nit) stage(it + S - 1, buf == 0 ? S - 1 : buf - 1);
     const int qt = qt_lo + it % nq;
 
-    const FA_LDS char* Qs = smem + buf * TILE;
-    const FA_LDS char* dOs = smem + (S + buf) * TILE;
-    const FA_LDS float* nls = (const FA_LDS float*)(smem + 2 * S * TILE + buf * VEC);
-    const FA_LDS float* dls = (const FA_LDS float*)(smem + 2 * S * TILE + (S + buf) * VEC);
-    const FA_LDS int* sqs = (const FA_LDS int*)(smem + 2 * S * TILE + (2 * S + buf) * VEC);
+    const int slot = buf * TEAMS + team;
+    const FA_LDS char* Qs = smem + slot * TILE;
+    const FA_LDS char* dOs = smem + OFF_DO + slot * TILE;
+    const FA_LDS float* nls = (const FA_LDS float*)(smem + OFF_NLS + slot * VEC);
+    const FA_LDS float* dls = (const FA_LDS float*)(smem + OFF_DLS + slot * VEC);
+    const FA_LDS int* sqs = (const FA_LDS int*)(smem + OFF_SEG + buf * VEC);
     const int q0 = qt * BMQ;
     const int qlast = min(q0 + BMQ, N) - 1;
 
@@ -461,6 +488,30 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     }
   }
 
+  if constexpr (TEAMS == 2) {
+    // team 0 += team 1, dK then dV, through the (now idle) ring: one fp32
+    // value per (key wave, accumulator element, lane), lane-contiguous
+    float* red = (float*)smem_raw;
+    auto exchange = [&](f32x16 (&acc)[DB]) {
+      __syncthreads();
+      if (team == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((kwave * DB + db) * 16 + r) * 64 + lane] = acc[db][r];
+      }
+      __syncthreads();
+      if (team == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] += red[((kwave * DB + db) * 16 + r) * 64 + lane];
+      }
+    };
+    exchange(dkacc);
+    exchange(dvacc);
+    if (team == 1) return;
+  }
   if (kj < N) {
     store_rows<T, D>((T*)p.dk + offkv, kj, dkacc, p.scale, lane);
     store_rows<T, D>((T*)p.dv + offkv, kj, dvacc, 1.f, lane);
@@ -499,6 +550,17 @@ hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int 
 }
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s) {
+  // grouped heads, dense bf16, 4 key waves and an even group: two teams
+  if (FA_KV_TEAMS && nw == 4 && p.G > 1 && p.G % 2 == 0 && dtype == 0 && p.seg == nullptr) {
+    const long long total = (long long)p.B * (p.H / p.G) * p.ntiles;
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(8 * 64), 0, s, p);
+      return hipGetLastError();
+    };
+    if (D == 128) return causal ? go(dkdv_kernel<bf16, 128, true, 8, 2>) : go(dkdv_kernel<bf16, 128, false, 8, 2>);
+    if (D == 96) return causal ? go(dkdv_kernel<bf16, 96, true, 8, 2>) : go(dkdv_kernel<bf16, 96, false, 8, 2>);
+    return causal ? go(dkdv_kernel<bf16, 64, true, 8, 2>) : go(dkdv_kernel<bf16, 64, false, 8, 2>);
+  }
   return dispatch(dtype, D, causal, nw, [&](auto t, auto d, auto c, auto w) {
     using T = typename decltype(t)::type;
     constexpr int DD = decltype(d)::value, NW = decltype(w)::value;

@@ -38,6 +38,11 @@ namespace fa {
 // MI355X, rings deeper than two stages gain nothing here (within 1 %), and
 // the dK/dV kernel, which runs at the 256-register limit, spills with three;
 // fp32 tiles (small shapes only) always use two stages and full waits.
+// Two-team dK/dV workgroups for grouped-query heads (see dkdv_kernel); 0
+// turns them off.
+#ifndef FA_KV_TEAMS
+#define FA_KV_TEAMS 1
+#endif
 #ifndef FA_FWD_STAGES
 #define FA_FWD_STAGES 2
 #endif
