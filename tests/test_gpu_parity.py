@@ -353,6 +353,29 @@ def test_grouped_query_heads_8k():
         assert bool((out[n] == again[n]).all()), f"{n} differs between identical runs"
 
 
+def test_maximum_sequence_length():
+    """The largest N the library accepts (FA_MAX_N = 2^22 tokens, one head,
+    D = 64: 512 MiB per tensor), packed as 1024 documents of 4096 tokens so
+    that the run stays short while every index, table and work list runs at
+    full size.  The first, a middle and the last document are each checked
+    against the oracle on that document alone (a packed row is each segment
+    on its own)."""
+    N, D, L = 1 << 22, 64, 4096
+    say(f"maximum length B1 H1 N{N} D{D} bf16, {N // L} documents of {L}")
+    t = workloads.make_tensors(1, 1, N, D, "bf16", 91)
+    seg = np.repeat(np.arange(N // L, dtype=np.int32), L)[None]
+    out = run_gpu(t, seg, "bf16", 0.125, True)
+    for d in (0, N // L // 2, N // L - 1):
+        r0, r1 = d * L, (d + 1) * L
+        say(f"  document {d}: rows {r0}..{r1 - 1}")
+        tb = {n: t[n][:, :, r0:r1] for n in t}
+        ref = _oracle_full(tb, None, 0.125, True)
+        check_o(down(out["o"][:, :, r0:r1]), ref["o"], "bf16")
+        check_lse(down(out["lse"][:, :, r0:r1]), ref["lse"], "bf16")
+        for n in ("dq", "dk", "dv"):
+            check_grad(down(out[n][:, :, r0:r1]), ref[n], "bf16", f"{n} document {d}")
+
+
 def test_head_dim_96_8k():
     """head_dim 96 at a full-size causal shape: one whole head against the
     oracle, sampled rows of every head, and the identities."""
