@@ -551,15 +551,17 @@ hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int 
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s) {
   // grouped heads, dense bf16, 4 key waves and an even group: two teams
-  if (FA_KV_TEAMS && nw == 4 && p.G > 1 && p.G % 2 == 0 && dtype == 0 && p.seg == nullptr) {
-    const long long total = (long long)p.B * (p.H / p.G) * p.ntiles;
-    auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(8 * 64), 0, s, p);
-      return hipGetLastError();
-    };
-    if (D == 128) return causal ? go(dkdv_kernel<bf16, 128, true, 8, 2>) : go(dkdv_kernel<bf16, 128, false, 8, 2>);
-    if (D == 96) return causal ? go(dkdv_kernel<bf16, 96, true, 8, 2>) : go(dkdv_kernel<bf16, 96, false, 8, 2>);
-    return causal ? go(dkdv_kernel<bf16, 64, true, 8, 2>) : go(dkdv_kernel<bf16, 64, false, 8, 2>);
+  if constexpr (FA_KV_TEAMS != 0) {
+    if (nw == 4 && p.G > 1 && p.G % 2 == 0 && dtype == 0 && p.seg == nullptr) {
+      const long long total = (long long)p.B * (p.H / p.G) * p.ntiles;
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(8 * 64), 0, s, p);
+        return hipGetLastError();
+      };
+      if (D == 128) return causal ? go(dkdv_kernel<bf16, 128, true, 8, 2>) : go(dkdv_kernel<bf16, 128, false, 8, 2>);
+      if (D == 96) return causal ? go(dkdv_kernel<bf16, 96, true, 8, 2>) : go(dkdv_kernel<bf16, 96, false, 8, 2>);
+      return causal ? go(dkdv_kernel<bf16, 64, true, 8, 2>) : go(dkdv_kernel<bf16, 64, false, 8, 2>);
+    }
   }
   return dispatch(dtype, D, causal, nw, [&](auto t, auto d, auto c, auto w) {
     using T = typename decltype(t)::type;
