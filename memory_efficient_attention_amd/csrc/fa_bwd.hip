@@ -255,15 +255,21 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
 // trip counts, shared barriers), and team 1 adds its dK and dV into team 0's
 // through LDS at the end.  That gives grouped heads full-occupancy
 // workgroups of equal halves instead of few long, half-occupied ones.
-template <typename T, int D, bool CAUSAL, int NW, int TEAMS = 1>
+//
+// QSUB = 2 (dense multi-head calls, 8 waves): each ring slot holds two query
+// tiles, walked one after the other with the same registers, so a wave does
+// twice the MFMAs per barrier.  The order of the MFMAs on every accumulator
+// is unchanged.
+template <typename T, int D, bool CAUSAL, int NW, int TEAMS = 1, int QSUB = 1>
 __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const BwdParams p) {
   constexpr int KW = NW / TEAMS;   // waves along the keys
   constexpr int BNK = KW * 32, BMQ = QRY_TILE;
   constexpr int KS = D / 16, DB = D / 32, QB = BMQ / 32;
+  constexpr int SR = QSUB * BMQ;   // query rows per ring slot
   using L = Layout<T, D>;
-  using St = Stager<T, BMQ, D, NW>;
-  constexpr int TILE = L::bytes(BMQ);
-  constexpr int VEC = BMQ * 4;
+  using St = Stager<T, SR, D, NW>;
+  constexpr int TILE = L::bytes(SR);
+  constexpr int VEC = SR * 4;
   constexpr int PER_STAGE = TEAMS * (2 * TILE + 2 * VEC) + VEC;
   constexpr int S = sizeof(T) == 2 ? stages_for(FA_DKV_STAGES, PER_STAGE, NW) : 2;
   static_assert(S >= 2 && S * PER_STAGE <= LDS_PER_CU, "Q/dO stages must fit in LDS");
@@ -324,11 +330,12 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   const T* gk = (const T*)p.k + offkv;
   const T* gv = (const T*)p.v + offkv;
   const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
-  // iteration it covers query head bh0 + team GT + it / nq, query tile
-  // qt_lo + it % nq (GT = G / TEAMS heads per team)
+  // iteration it covers query head bh0 + team GT + it / nqs, query tiles
+  // qt_lo + QSUB (it % nqs) .. + QSUB - 1 (GT = G / TEAMS heads per team)
   const int GT = G / TEAMS;
   const int nq = qt_hi - qt_lo + 1;
-  const int nit = nq > 0 ? GT * nq : 0;
+  const int nqs = (nq + QSUB - 1) / QSUB;
+  const int nit = nq > 0 ? GT * nqs : 0;
 
   const int k0 = kt * BNK;
   const int kw0 = k0 + kwave * 32;
@@ -369,18 +376,18 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   }
 
   auto stage = [&](int it, int buf) {
-    const int hj = it / nq;
-    const int r0 = (qt_lo + it - hj * nq) * BMQ;
+    const int hj = it / nqs;
+    const int r0 = (qt_lo + (it - hj * nqs) * QSUB) * BMQ;
 #pragma unroll
     for (int t = 0; t < TEAMS; ++t) {
       const size_t bh = bh0 + t * GT + hj;
       const int slot = buf * TEAMS + t;
       (SHARE || t == 0 ? stq : stq2).issue(smem + slot * TILE, (const T*)p.q + bh * N * D, r0, N);
       (SHARE ? stq : (t == 0 ? stdo : stdo2)).issue(smem + OFF_DO + slot * TILE, (const T*)p.dO + bh * N * D, r0, N);
-      stage_vec<BMQ>(smem + OFF_NLS + slot * VEC, p.nls + bh * N, r0, N, wave, (2 * t) % NW, lane);
-      stage_vec<BMQ>(smem + OFF_DLS + slot * VEC, p.delta + bh * N, r0, N, wave, (2 * t + 1) % NW, lane);
+      stage_vec<SR>(smem + OFF_NLS + slot * VEC, p.nls + bh * N, r0, N, wave, (2 * t) % NW, lane);
+      stage_vec<SR>(smem + OFF_DLS + slot * VEC, p.delta + bh * N, r0, N, wave, (2 * t + 1) % NW, lane);
     }
-    if (packed) stage_vec<BMQ>(smem + OFF_SEG + buf * VEC, seg, r0, N, wave, (2 * TEAMS) % NW, lane);
+    if (packed) stage_vec<SR>(smem + OFF_SEG + buf * VEC, seg, r0, N, wave, (2 * TEAMS) % NW, lane);
   };
 
   // Ring of S stages, as in the forward.
@@ -400,7 +407,6 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     wait_tiles<LPT, S - 2>(nit - 1 - it);
     __syncthreads();
     if (it + S - 1 < nit) stage(it + S - 1, buf == 0 ? S - 1 : buf - 1);
-    const int qt = qt_lo + it % nq;
 
     const int slot = buf * TEAMS + team;
     const FA_LDS char* Qs = smem + slot * TILE;
@@ -408,6 +414,12 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     const FA_LDS float* nls = (const FA_LDS float*)(smem + OFF_NLS + slot * VEC);
     const FA_LDS float* dls = (const FA_LDS float*)(smem + OFF_DLS + slot * VEC);
     const FA_LDS int* sqs = (const FA_LDS int*)(smem + OFF_SEG + buf * VEC);
+    const int qtb = qt_lo + (it % nqs) * QSUB;
+#pragma unroll
+    for (int sub = 0; sub < QSUB; ++sub) {
+    const int qt = qtb + sub;
+    if (qt > qt_hi) break;
+    const int rs = 32 * QB * sub;   // first row of this query tile in the slot
     const int q0 = qt * BMQ;
     const int qlast = min(q0 + BMQ, N) - 1;
 
@@ -415,7 +427,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     if (CAUSAL) skip = skip || qlast < kw0;
     bool full = (q0 + BMQ <= N) && (kw0 + 31 < N) && (!CAUSAL || q0 >= kw0 + 31);
     if (packed) {
-      const int sq0 = sqs[0], sql = sqs[qlast - q0];
+      const int sq0 = sqs[rs], sql = sqs[rs + qlast - q0];
       skip = skip || sq0 > segk_last || (!CAUSAL && sql < segk_first);
       full = full && (min(sq0, segk_first) == max(sql, segk_last));
     }
@@ -429,8 +441,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 nl = *(const FA_LDS f32x4*)(nls + 32 * qb + 8 * j + 4 * h);
-        const f32x4 nd = *(const FA_LDS f32x4*)(dls + 32 * qb + 8 * j + 4 * h);
+        const f32x4 nl = *(const FA_LDS f32x4*)(nls + rs + 32 * qb + 8 * j + 4 * h);
+        const f32x4 nd = *(const FA_LDS f32x4*)(dls + rs + 32 * qb + 8 * j + 4 * h);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sacc[qb][4 * j + i] = nl[i];
@@ -439,8 +451,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        mma(sacc[qb], frag_row<T, D>(Qs, rbase, 32 * qb, ks), kf[ks]);
-        mma(dpacc[qb], frag_row<T, D>(dOs, rbase, 32 * qb, ks), vf[ks]);
+        mma(sacc[qb], frag_row<T, D>(Qs, rbase, rs + 32 * qb, ks), kf[ks]);
+        mma(dpacc[qb], frag_row<T, D>(dOs, rbase, rs + 32 * qb, ks), vf[ks]);
       }
     }
 
@@ -451,7 +463,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int qr = 32 * qb + 8 * j + 4 * h;
-          const i32x4 sq = packed ? *(const FA_LDS i32x4*)(sqs + qr) : i32x4{0, 0, 0, 0};
+          const i32x4 sq = packed ? *(const FA_LDS i32x4*)(sqs + rs + qr) : i32x4{0, 0, 0, 0};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int q = q0 + qr + i;
@@ -482,9 +494,10 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          mma(dvacc[db], frag_col<T, D>(dOs, cbase, 32 * qb + 16 * kc, 32 * db), pf[kc]);
-          mma(dkacc[db], frag_col<T, D>(Qs, cbase, 32 * qb + 16 * kc, 32 * db), dsf[kc]);
+          mma(dvacc[db], frag_col<T, D>(dOs, cbase, rs + 32 * qb + 16 * kc, 32 * db), pf[kc]);
+          mma(dkacc[db], frag_col<T, D>(Qs, cbase, rs + 32 * qb + 16 * kc, 32 * db), dsf[kc]);
         }
+    }
     }
   }
 
@@ -568,7 +581,10 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, in
     constexpr int DD = decltype(d)::value, NW = decltype(w)::value;
     constexpr bool C = decltype(c)::value;
     const long long total = (long long)p.B * (p.H / p.G) * p.ntiles;
-    hipLaunchKernelGGL((dkdv_kernel<T, DD, C, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    // 8-wave dK/dV workgroups are dense multi-head ones (packed and grouped
+    // calls use 4): two query tiles per ring slot for bf16
+    constexpr int QS = (NW == 8 && sizeof(T) == 2) ? FA_DKV_QSUB : 1;
+    hipLaunchKernelGGL((dkdv_kernel<T, DD, C, NW, 1, QS>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
   });
 }
