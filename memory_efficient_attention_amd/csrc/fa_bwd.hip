@@ -66,21 +66,27 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
 // see.  Per tile: S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T held in registers),
 // P^T and dS^T in registers, dQ^T += K^T dS^T with K^T through the transposing
 // LDS read of the K tile.
+//
+// KSUB = 2 (8-wave bf16 workgroups): each ring slot holds two key tiles,
+// walked one after the other with the same registers, so a wave does twice
+// the MFMAs per barrier; the MFMA order on every accumulator is unchanged.
 template <typename T, int D, bool CAUSAL, int NW>
 __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdParams p) {
   constexpr int BM = NW * 32, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
+  constexpr int KSUB = (NW == 8 && sizeof(T) == 2) ? FA_KSUB : 1;
+  constexpr int SR = KSUB * BN;   // key rows per ring slot
   // K is read along rows and transposed (DUAL), V only along rows.
   using LK = Layout<T, D, true>;
   using LV = Layout<T, D, false>;
-  using StK = Stager<T, BN, D, NW, true>;
-  using StV = Stager<T, BN, D, NW, false>;
-  constexpr int TK = LK::bytes(BN), TV = LV::bytes(BN);
-  constexpr int S = sizeof(T) == 2 ? stages_for(FA_DQ_STAGES, TK + TV + BN * 4, NW) : 2;
-  static_assert(S >= 2 && S * (TK + TV + BN * 4) <= LDS_PER_CU, "K/V stages must fit in LDS");
+  using StK = Stager<T, SR, D, NW, true>;
+  using StV = Stager<T, SR, D, NW, false>;
+  constexpr int TK = LK::bytes(SR), TV = LV::bytes(SR);
+  constexpr int S = sizeof(T) == 2 ? stages_for(FA_DQ_STAGES, TK + TV + SR * 4, NW) : 2;
+  static_assert(S >= 2 && S * (TK + TV + SR * 4) <= LDS_PER_CU, "K/V stages must fit in LDS");
   constexpr int LPT = (StK::NINST + StV::NINST) / NW;
   // layout: K[S] | V[S] | seg[S]
-  __shared__ __attribute__((aligned(1024))) char smem_raw[S * (TK + TV + BN * 4)];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[S * (TK + TV + SR * 4)];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -148,16 +154,19 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
 
-  auto stage = [&](int kt, int buf) {
-    stk.issue(smem + buf * TK, gk, kt * BN, N);
-    stv.issue(smem + S * TK + buf * TV, gv, kt * BN, N);
-    if (packed) stage_vec<BN>(smem + S * (TK + TV) + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
+  // ring slot j holds key tiles kt_lo + KSUB j .. + KSUB - 1
+  const int nst = (kt_hi - kt_lo + KSUB) / KSUB;
+  auto stage = [&](int j, int buf) {
+    const int r0 = (kt_lo + KSUB * j) * BN;
+    stk.issue(smem + buf * TK, gk, r0, N);
+    stv.issue(smem + S * TK + buf * TV, gv, r0, N);
+    if (packed) stage_vec<SR>(smem + S * (TK + TV) + buf * SR * 4, seg, r0, N, wave, NW - 1, lane);
   };
 
   // Ring of S stages, as in the forward.
 #pragma unroll
   for (int i = 0; i < S - 1; ++i)
-    if (kt_lo + i <= kt_hi) stage(kt_lo + i, i);
+    if (i < nst) stage(i, i);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     settle(qf[ks]);
@@ -168,15 +177,21 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
   settle(segq);
   settle(segq_first);
   settle(segq_last);
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int buf = (kt - kt_lo) % S;
-    wait_tiles<LPT, S - 2>(kt_hi - kt);
+  for (int js = 0; js < nst; ++js) {
+    const int buf = js % S;
+    wait_tiles<LPT, S - 2>(nst - 1 - js);
     __syncthreads();
-    if (kt + S - 1 <= kt_hi) stage(kt + S - 1, buf == 0 ? S - 1 : buf - 1);
+    if (js + S - 1 < nst) stage(js + S - 1, buf == 0 ? S - 1 : buf - 1);
 
     const FA_LDS char* Ks = smem + buf * TK;
     const FA_LDS char* Vs = smem + S * TK + buf * TV;
-    const FA_LDS int* segk = (const FA_LDS int*)(smem + S * (TK + TV) + buf * BN * 4);
+    const FA_LDS int* segs = (const FA_LDS int*)(smem + S * (TK + TV) + buf * SR * 4);
+#pragma unroll
+    for (int sub = 0; sub < KSUB; ++sub) {
+    const int kt = kt_lo + KSUB * js + sub;
+    if (kt > kt_hi) break;
+    const int rs = BN * sub;   // first row of this key tile in the slot
+    const FA_LDS int* segk = segs + rs;
     const int k0 = kt * BN;
     const int klast = min(k0 + BN, N) - 1;
 
@@ -200,8 +215,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        mma(sacc[kb], frag_row<T, D, true>(Ks, kbase_r, 32 * kb, ks), qf[ks]);
-        mma(dpacc[kb], frag_row<T, D, false>(Vs, vbase_r, 32 * kb, ks), dof[ks]);
+        mma(sacc[kb], frag_row<T, D, true>(Ks, kbase_r, rs + 32 * kb, ks), qf[ks]);
+        mma(dpacc[kb], frag_row<T, D, false>(Vs, vbase_r, rs + 32 * kb, ks), dof[ks]);
       }
     }
 
@@ -237,7 +252,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
-          mma(dqacc[db], frag_col<T, D>(Ks, cbase, 32 * kb + 16 * kc, 32 * db), dsf[kb][kc]);
+          mma(dqacc[db], frag_col<T, D>(Ks, cbase, rs + 32 * kb + 16 * kc, 32 * db), dsf[kb][kc]);
+    }
   }
 
   if (qi < N) store_rows<T, D>((T*)p.dq + off, qi, dqacc, p.scale, lane);

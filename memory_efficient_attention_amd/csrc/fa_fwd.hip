@@ -24,21 +24,28 @@
 
 namespace fa {
 
+//
+// KSUB = 2 (8-wave bf16 workgroups): each ring slot holds two key tiles,
+// walked one after the other with the same registers, so a wave does twice
+// the MFMAs per barrier; every operation on every row happens in the same
+// order as with one tile per slot.
 template <typename T, int D, bool CAUSAL, int NW>
 __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const FwdParams p) {
   constexpr int BM = NW * 32, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
+  constexpr int KSUB = (NW == 8 && sizeof(T) == 2) ? FA_KSUB : 1;
+  constexpr int SR = KSUB * BN;   // key rows per ring slot
   // K is read only along rows (row-only layout), V only transposed (DUAL).
   using LK = Layout<T, D, false>;
   using LV = Layout<T, D, true>;
-  using StK = Stager<T, BN, D, NW, false>;
-  using StV = Stager<T, BN, D, NW, true>;
-  constexpr int TK = LK::bytes(BN), TV = LV::bytes(BN);
-  constexpr int S = sizeof(T) == 2 ? stages_for(FA_FWD_STAGES, TK + TV + BN * 4, NW) : 2;
-  static_assert(S >= 2 && S * (TK + TV + BN * 4) <= LDS_PER_CU, "K/V stages must fit in LDS");
-  constexpr int LPT = (StK::NINST + StV::NINST) / NW;   // loads per wave per tile, at least
+  using StK = Stager<T, SR, D, NW, false>;
+  using StV = Stager<T, SR, D, NW, true>;
+  constexpr int TK = LK::bytes(SR), TV = LV::bytes(SR);
+  constexpr int S = sizeof(T) == 2 ? stages_for(FA_FWD_STAGES, TK + TV + SR * 4, NW) : 2;
+  static_assert(S >= 2 && S * (TK + TV + SR * 4) <= LDS_PER_CU, "K/V stages must fit in LDS");
+  constexpr int LPT = (StK::NINST + StV::NINST) / NW;   // loads per wave per slot, at least
   // layout: K[S] | V[S] | seg[S]
-  __shared__ __attribute__((aligned(1024))) char smem_raw[S * (TK + TV + BN * 4)];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[S * (TK + TV + SR * 4)];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -106,32 +113,41 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
   float msc = -INFINITY, lsum = 0.f;
   const float c = p.c;
 
-  auto stage = [&](int kt, int buf) {
-    stk.issue(smem + buf * TK, gk, kt * BN, N);
-    stv.issue(smem + S * TK + buf * TV, gv, kt * BN, N);
-    if (packed) stage_vec<BN>(smem + S * (TK + TV) + buf * BN * 4, seg, kt * BN, N, wave, NW - 1, lane);
+  // ring slot j holds key tiles kt_lo + KSUB j .. + KSUB - 1
+  const int nst = (kt_hi - kt_lo + KSUB) / KSUB;
+  auto stage = [&](int j, int buf) {
+    const int r0 = (kt_lo + KSUB * j) * BN;
+    stk.issue(smem + buf * TK, gk, r0, N);
+    stv.issue(smem + S * TK + buf * TV, gv, r0, N);
+    if (packed) stage_vec<SR>(smem + S * (TK + TV) + buf * SR * 4, seg, r0, N, wave, NW - 1, lane);
   };
-  // Ring of S stages: tiles kt + 1 .. kt + S - 2 stay in flight while tile kt
+  // Ring of S stages: slots j + 1 .. j + S - 2 stay in flight while slot j
   // is used; the barrier after the wait also tells every wave that the
-  // buffer of tile kt - 1 is free for tile kt + S - 1.
+  // buffer of slot j - 1 is free for slot j + S - 1.
 #pragma unroll
   for (int i = 0; i < S - 1; ++i)
-    if (kt_lo + i <= kt_hi) stage(kt_lo + i, i);
+    if (i < nst) stage(i, i);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
   settle(segq);
   settle(segq_first);
   settle(segq_last);
 
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int buf = (kt - kt_lo) % S;
-    wait_tiles<LPT, S - 2>(kt_hi - kt);
+  for (int js = 0; js < nst; ++js) {
+    const int buf = js % S;
+    wait_tiles<LPT, S - 2>(nst - 1 - js);
     __syncthreads();
-    if (kt + S - 1 <= kt_hi) stage(kt + S - 1, buf == 0 ? S - 1 : buf - 1);
+    if (js + S - 1 < nst) stage(js + S - 1, buf == 0 ? S - 1 : buf - 1);
 
     const FA_LDS char* Ks = smem + buf * TK;
     const FA_LDS char* Vs = smem + S * TK + buf * TV;
-    const FA_LDS int* segk = (const FA_LDS int*)(smem + S * (TK + TV) + buf * BN * 4);
+    const FA_LDS int* segs = (const FA_LDS int*)(smem + S * (TK + TV) + buf * SR * 4);
+#pragma unroll
+    for (int sub = 0; sub < KSUB; ++sub) {
+    const int kt = kt_lo + KSUB * js + sub;
+    if (kt > kt_hi) break;
+    const int rs = BN * sub;   // first row of this key tile in the slot
+    const FA_LDS int* segk = segs + rs;
     const int k0 = kt * BN;
     const int klast = min(k0 + BN, N) - 1;
 
@@ -153,7 +169,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
     for (int kb = 0; kb < KB; ++kb) {
       sacc[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma(sacc[kb], frag_row<T, D, false>(Ks, rbase, 32 * kb, ks), qf[ks]);
+      for (int ks = 0; ks < KS; ++ks) mma(sacc[kb], frag_row<T, D, false>(Ks, rbase, rs + 32 * kb, ks), qf[ks]);
     }
     if (!full) {
 #pragma unroll
@@ -241,7 +257,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
-          mma(oacc[db], frag_col<T, D>(Vs, cbase, 32 * kb + 16 * kc, 32 * db), pf[kb][kc]);
+          mma(oacc[db], frag_col<T, D>(Vs, cbase, rs + 32 * kb + 16 * kc, 32 * db), pf[kb][kc]);
+    }
   }
 
   const float lt = lsum + other_half(lsum);

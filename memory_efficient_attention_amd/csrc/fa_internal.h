@@ -43,6 +43,10 @@ namespace fa {
 #ifndef FA_KV_TEAMS
 #define FA_KV_TEAMS 1
 #endif
+// Key tiles per ring slot in 8-wave bf16 forward and dQ workgroups (1 or 2).
+#ifndef FA_KSUB
+#define FA_KSUB 2
+#endif
 // Query tiles per ring slot in dense multi-head 8-wave dK/dV (1 or 2).
 #ifndef FA_DKV_QSUB
 #define FA_DKV_QSUB 2
