@@ -58,9 +58,6 @@ constexpr int STAGES = FA_LCE_STAGES;
 static_assert(WM == 64 || WM == 128, "per-wave block");
 static_assert(STAGES >= 2 && STAGES <= 4, "stage ring");
 static_assert(TK == 32 || TK == 64, "contraction slice");
-#ifndef FA_LCE_FENCE
-#define FA_LCE_FENCE 1
-#endif
 using LRow = Layout<bf16, TK, false>;     // 256 rows x TK elements
 using LCol = Layout<bf16, TM, true>;      // TK rows x 256 elements (transposed reads)
 using StRow = Stager<bf16, TM, TK, NWV, false>;
@@ -157,9 +154,6 @@ __device__ __forceinline__ void gemm_tile(FA_LDS char* smem, int nk, SA&& stage_
     buf = buf + 1 == STAGES ? 0 : buf + 1;
     bf16x8 a[MB], b[NB];
     read(ta, tb, 0, a, b);
-    // keep the reads ahead of the deferred MFMAs (the scheduler would
-    // otherwise hoist the MFMAs, which then block the reads' issue)
-    if (FA_LCE_FENCE) __builtin_amdgcn_sched_barrier(0);
     if (s > 0) mmas(pa, pb);
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks) {
