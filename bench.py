@@ -366,7 +366,9 @@ def report_all(args):
     print("|---|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
         s = r["stages"]
-        sp = (f"{r['speedup_vs_causal']:.2f}x ({r['visible_ratio']:.2f}x)" if "speedup_vs_causal" in r else "")
+        sp = (f"{r['speedup_vs_causal']:.2f}x ({r['visible_ratio']:.2f}x) against causal {r['causal_ms']:.3f} ms "
+              f"({14 * r['causal_V'] * workloads.get(r['workload']).D / (r['causal_ms'] * 1e-3) / 1e12:.0f} TFLOP/s)"
+              if "speedup_vs_causal" in r else "")
         if "cold_ms" in r:
             sp += f"; cache-cold {r['cold_ms']:.3f} ms"
         print(f"| {r['workload']} | {r['ms']:.3f} | {r['ms_median']:.3f} | {r['ms_min']:.3f} | {s['fwd']:.3f} | "
