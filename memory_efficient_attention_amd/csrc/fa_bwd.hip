@@ -220,25 +220,37 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
       }
     }
 
+    if (!full) {
+      // Element 4j + i of block kb is key k0 + 4h + c with c = 32kb + 8j + i
+      // a compile-time constant: key < N and (causal) key <= qi become one
+      // compare of c against a per-lane bound; packed rows add the segment
+      // test on a branch of their own.
+      const int L = (CAUSAL ? min(qi, N - 1) : N - 1) - (k0 + 4 * h);
+      if (packed) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kr = 32 * kb + 8 * j + 4 * h;
-        i32x4 sk = (packed && !full) ? *(const FA_LDS i32x4*)(segk + kr) : i32x4{0, 0, 0, 0};
+          for (int j = 0; j < 4; ++j) {
+            const i32x4 sk = *(const FA_LDS i32x4*)(segk + 32 * kb + 8 * j + 4 * h);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s = sacc[kb][4 * j + i];
-          if (!full) {
-            const int key = k0 + kr + i;
-            const bool vis = key < N && (!CAUSAL || key <= qi) && (!packed || sk[i] == segq);
-            if (!vis) s = -INFINITY;
+            for (int i = 0; i < 4; ++i)
+              if (!(32 * kb + 8 * j + i <= L && sk[i] == segq)) sacc[kb][4 * j + i] = -INFINITY;
           }
-          const float pv = exp2_fast(fmaf(s, c, nlse2));
-          sacc[kb][4 * j + i] = pv * (dpacc[kb][4 * j + i] + ndlt);
-        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!(32 * kb + 8 * (r >> 2) + (r & 3) <= L)) sacc[kb][r] = -INFINITY;
       }
     }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = exp2_fast(fmaf(sacc[kb][r], c, nlse2));
+        sacc[kb][r] = pv * (dpacc[kb][r] + ndlt);
+      }
 
     frag_t<T> dsf[KB][2];
 #pragma unroll
@@ -473,20 +485,41 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     }
 
     if (!full) {
-      // accumulator element 4j + i of block qb: query 32qb + 8j + 4h + i, key kj
+      // Accumulator element 4j + i of block qb: query q0 + 4h + c with
+      // c = 32qb + 8j + i a compile-time constant, key kj.  Visible iff
+      // kj < N, (causal) q >= kj and q < N: one compare of c against a
+      // per-lane lower bound, a second one only in the tile that holds row
+      // N - 1, and the segment test on a branch of packed rows.
+      const int base = q0 + 4 * h;
+      const int A = kj < N ? (CAUSAL ? kj : 0) - base : (1 << 30);   // c >= A
+      const int Bq = N - 1 - base;                                      // c <= Bq
+      const bool tail = q0 + BMQ > N;
+      if (packed) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int qr = 32 * qb + 8 * j + 4 * h;
-          const i32x4 sq = packed ? *(const FA_LDS i32x4*)(sqs + rs + qr) : i32x4{0, 0, 0, 0};
+          for (int j = 0; j < 4; ++j) {
+            const i32x4 sq = *(const FA_LDS i32x4*)(sqs + rs + 32 * qb + 8 * j + 4 * h);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int q = q0 + qr + i;
-            const bool v = q < N && kj < N && (!CAUSAL || kj <= q) && (!packed || sq[i] == segk);
-            if (!v) sacc[qb][4 * j + i] = -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+              const int cc = 32 * qb + 8 * j + i;
+              if (!(cc >= A && cc <= Bq && sq[i] == segk)) sacc[qb][4 * j + i] = -INFINITY;
+            }
           }
-        }
+      } else if (tail) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int cc = 32 * qb + 8 * (r >> 2) + (r & 3);
+            if (!(cc >= A && cc <= Bq)) sacc[qb][r] = -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!(32 * qb + 8 * (r >> 2) + (r & 3) >= A)) sacc[qb][r] = -INFINITY;
       }
     }
 

@@ -172,19 +172,27 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
       for (int ks = 0; ks < KS; ++ks) mma(sacc[kb], frag_row<T, D, false>(Ks, rbase, rs + 32 * kb, ks), qf[ks]);
     }
     if (!full) {
+      // Element 4j + i of block kb is key k0 + 4h + c with c = 32kb + 8j + i
+      // a compile-time constant: key < N and (causal) key <= qi become one
+      // compare of c against a per-lane bound; packed rows add the segment
+      // test on a branch of their own.
+      const int L = (CAUSAL ? min(qi, N - 1) : N - 1) - (k0 + 4 * h);
+      if (packed) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kr = 32 * kb + 8 * j + 4 * h;
-          const i32x4 sk = packed ? *(const FA_LDS i32x4*)(segk + kr) : i32x4{0, 0, 0, 0};
+          for (int j = 0; j < 4; ++j) {
+            const i32x4 sk = *(const FA_LDS i32x4*)(segk + 32 * kb + 8 * j + 4 * h);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = k0 + kr + i;
-            const bool vis = key < N && (!CAUSAL || key <= qi) && (!packed || sk[i] == segq);
-            if (!vis) sacc[kb][4 * j + i] = -INFINITY;
+            for (int i = 0; i < 4; ++i)
+              if (!(32 * kb + 8 * j + i <= L && sk[i] == segq)) sacc[kb][4 * j + i] = -INFINITY;
           }
-        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!(32 * kb + 8 * (r >> 2) + (r & 3) <= L)) sacc[kb][r] = -INFINITY;
       }
     }
 
