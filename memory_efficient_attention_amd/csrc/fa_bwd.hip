@@ -70,11 +70,11 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
 // KSUB = 2 (8-wave bf16 workgroups): each ring slot holds two key tiles,
 // walked one after the other with the same registers, so a wave does twice
 // the MFMAs per barrier; the MFMA order on every accumulator is unchanged.
-template <typename T, int D, bool CAUSAL, int NW>
+template <typename T, int D, bool CAUSAL, int NW, int KSUB = 1>
 __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdParams p) {
   constexpr int BM = NW * 32, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
-  constexpr int KSUB = (NW == 8 && sizeof(T) == 2) ? FA_KSUB : 1;
+  static_assert(KSUB == 1 || (KSUB == 2 && NW == 8 && sizeof(T) == 2), "two-tile slots: 8-wave bf16");
   constexpr int SR = KSUB * BN;   // key rows per ring slot
   // K is read along rows and transposed (DUAL), V only along rows.
   using LK = Layout<T, D, true>;
@@ -95,8 +95,10 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
   const int N = p.N;
   const int nqt = p.ntiles;
 
-  // (batch, head, query tile) and key-tile range, as in the forward.
-  const bool packed = p.seg != nullptr;
+  // (batch, head, query tile) and key-tile range, as in the forward.  Two-
+  // tile instances are launched for dense calls only, so they carry no
+  // packed code.
+  const bool packed = KSUB == 1 && p.seg != nullptr;
   int bh, b, qt, kt_lo = 0, kt_hi;
   if (packed) {
     const int4 wk = p.work[blockIdx.x / p.H];
@@ -328,7 +330,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   // causal, seen by the most queries) first.  The workgroup walks the query
   // tiles of each of the key/value head's G query heads in turn and sums
   // their contributions to dK and dV in its registers.
-  const bool packed = p.seg != nullptr;
+  // Two-tile instances are launched for dense calls only (no packed code).
+  const bool packed = QSUB == 1 && p.seg != nullptr;
   const int G = p.G, Hkv = p.H / G;
   int bg, b, kt, qt_lo, qt_hi;
   if (packed) {
@@ -490,11 +493,9 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
       // kj < N, (causal) q >= kj and q < N: one compare of c against a
       // per-lane lower bound, a second one only in the tile that holds row
       // N - 1, and the segment test on a branch of packed rows.
-      const int base = q0 + 4 * h;
-      const int A = kj < N ? (CAUSAL ? kj : 0) - base : (1 << 30);   // c >= A
-      const int Bq = N - 1 - base;                                      // c <= Bq
-      const bool tail = q0 + BMQ > N;
+      const int A = kj < N ? (CAUSAL ? kj : 0) - (q0 + 4 * h) : (1 << 30);   // c >= A
       if (packed) {
+        const int Bq = N - 1 - (q0 + 4 * h);   // c <= Bq
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -506,7 +507,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
               if (!(cc >= A && cc <= Bq && sq[i] == segk)) sacc[qb][4 * j + i] = -INFINITY;
             }
           }
-      } else if (tail) {
+      } else if (q0 + BMQ > N) {   // the tile holding row N - 1
+        const int Bq = N - 1 - (q0 + 4 * h);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -606,7 +608,11 @@ hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int 
     constexpr int DD = decltype(d)::value, NW = decltype(w)::value;
     constexpr bool C = decltype(c)::value;
     const long long total = (long long)p.B * p.H * p.ntiles;
-    hipLaunchKernelGGL((dq_kernel<T, DD, C, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    constexpr int KS2 = (NW == 8 && sizeof(T) == 2) ? FA_KSUB : 1;
+    if (KS2 > 1 && p.seg == nullptr)
+      hipLaunchKernelGGL((dq_kernel<T, DD, C, NW, KS2>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((dq_kernel<T, DD, C, NW, 1>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
   });
 }
@@ -633,7 +639,10 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, in
     // 8-wave dK/dV workgroups are dense multi-head ones (packed and grouped
     // calls use 4): two query tiles per ring slot for bf16
     constexpr int QS = (NW == 8 && sizeof(T) == 2) ? FA_DKV_QSUB : 1;
-    hipLaunchKernelGGL((dkdv_kernel<T, DD, C, NW, 1, QS>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    if (QS > 1 && p.seg == nullptr)
+      hipLaunchKernelGGL((dkdv_kernel<T, DD, C, NW, 1, QS>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<T, DD, C, NW, 1, 1>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
   });
 }
