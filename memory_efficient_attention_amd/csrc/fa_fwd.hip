@@ -202,22 +202,24 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
     // references to the tile's row maxima, rescales O and the sums, and
     // recomputes the probabilities.  Both lanes of a row see the same row
     // max, so they take the same decisions.
+    // A wave with a row that has no reference yet (its first visible tile)
+    // takes the rare path anyway, so it skips the optimistic pass.
     float ptile[KB][16];
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
-    {
-      const float mref = (msc == -INFINITY) ? 0.f : msc;
+    bool trigger = __builtin_amdgcn_ballot_w64(msc == -INFINITY) != 0;
+    if (!trigger) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2_fast(fmaf(sacc[kb][r], c, -mref));
+          const float e = exp2_fast(fmaf(sacc[kb][r], c, -msc));
           ptile[kb][r] = e;
           ls[r & 3] += e;
         }
+      const float lpart = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      trigger = __builtin_amdgcn_ballot_w64(!(lpart < GROW_LIMIT)) != 0;
     }
-    const float lpart = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    const bool trigger = msc == -INFINITY || !(lpart < GROW_LIMIT);
-    if (__builtin_amdgcn_ballot_w64(trigger) != 0) {
+    if (trigger) {
       float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
