@@ -65,6 +65,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 // Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
 std::mutex g_mu;
 signed char g_dev_ok[64];
+int g_dev_cus[64];   // compute units of each checked device
 
 fa_status device_ok() {
   int dev = -1;
@@ -85,9 +86,31 @@ fa_status device_ok() {
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   if (dev < 64) {
     std::lock_guard<std::mutex> lk(g_mu);
+    g_dev_cus[dev] = prop.multiProcessorCount;
     g_dev_ok[dev] = ok ? 1 : 2;
   }
   return ok ? FA_OK : FA_ERR_DEVICE;
+}
+
+// Compute units of the current device once device_ok() has passed (0 if
+// unknown, which turns the one-round balancing off).
+int device_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_dev_cus[dev];
+}
+
+// Mirrored 32-row blocks (mirror_block in the kernels) for a dense causal
+// launch of `wgs` workgroups of `nw` waves over N rows, when the blocks tile
+// N exactly and the grid needs at most two rounds of the chip's CUs.  Up to
+// there the heaviest workgroups set the step time; on larger grids the
+// heaviest-first order packs unequal workgroups as well or better.
+int use_mirror(bool dense, int causal, int N, int nw, long long wgs) {
+  return dense && causal && N % (nw * 32) == 0 && wgs <= 2LL * device_cus() ? 1 : 0;
 }
 
 fa_status common_checks(int B, int H, int Hkv, int N, int D, fa_dtype dtype, float scale) {
@@ -143,6 +166,7 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   const int nw = fa::tile_config(seg != nullptr, Hkv != H).nw_q;
   const int bm = nw * 32;   // queries per workgroup
   p.nqt = (N + bm - 1) / bm;
+  p.mirror = use_mirror(seg == nullptr, causal, N, nw, (long long)B * H * p.nqt);
   p.scale = scale;
   p.c = log2e_scale(scale);
   if (seg) {
@@ -233,11 +257,14 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   if (!record(events, 1, s)) return FA_ERR_HIP;
   p.work = seg ? (const int4*)(w + L.kwork) : nullptr;
   p.ntiles = ntiles_kv;
+  // key blocks mirror in the one-team kernel of ungrouped heads only
+  p.mirror = use_mirror(seg == nullptr && Hkv == H, causal, N, nw_kv, (long long)B * Hkv * ntiles_kv);
   if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, nw_kv, s) != hipSuccess) return FA_ERR_HIP;
 
   if (!record(events, 2, s)) return FA_ERR_HIP;
   p.work = seg ? (const int4*)(w + L.qwork) : nullptr;
   p.ntiles = ntiles;
+  p.mirror = use_mirror(seg == nullptr, causal, N, nw, (long long)B * H * ntiles);
   if (fa::launch_bwd_dq(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
   if (!record(events, 3, s)) return FA_ERR_HIP;
   return FA_OK;

@@ -99,20 +99,27 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
   // tile instances are launched for dense calls only, so they carry no
   // packed code.
   const bool packed = KSUB == 1 && p.seg != nullptr;
-  int bh, b, qt, kt_lo = 0, kt_hi;
+  int bh, b, kt_lo = 0, kt_hi, qw0;
   if (packed) {
     const int4 wk = p.work[blockIdx.x / p.H];
     b = wk.x;
-    qt = wk.y;
+    qw0 = wk.y * BM + wave * 32;
     kt_lo = wk.z;
     kt_hi = wk.w;
     bh = b * p.H + (int)(blockIdx.x % p.H);
   } else {
     const int Lw = xcd_remap(blockIdx.x, p.B * p.H * nqt);
     bh = Lw / nqt;
-    qt = nqt - 1 - (Lw - bh * nqt);
     b = bh / p.H;
-    kt_hi = ((CAUSAL ? min(qt * BM + BM, N) : N) - 1) / BN;
+    if (CAUSAL && p.mirror) {
+      const int t = Lw - bh * nqt;
+      qw0 = 32 * mirror_block(t, wave, NW, nqt);
+      kt_hi = (32 * (nqt * NW - t * (NW / 2)) - 1) / BN;
+    } else {
+      const int qt = nqt - 1 - (Lw - bh * nqt);
+      qw0 = qt * BM + wave * 32;
+      kt_hi = ((CAUSAL ? min(qt * BM + BM, N) : N) - 1) / BN;
+    }
   }
   const size_t off = (size_t)bh * N * D;
   const size_t offkv = (size_t)(bh / p.G) * N * D;   // its key/value head
@@ -122,8 +129,6 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
   const T* gdo = (const T*)p.dO + off;
   const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
 
-  const int q0 = qt * BM;
-  const int qw0 = q0 + wave * 32;
   const int qi = qw0 + col;
   const int qc = min(qi, N - 1);
   const int qlast = min(qw0 + 31, N - 1);
@@ -333,14 +338,24 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   // Two-tile instances are launched for dense calls only (no packed code).
   const bool packed = QSUB == 1 && p.seg != nullptr;
   const int G = p.G, Hkv = p.H / G;
-  int bg, b, kt, qt_lo, qt_hi;
+  int bg, b, qt_lo, qt_hi, kw0;
   if (packed) {
     const int4 wk = p.work[blockIdx.x / Hkv];
     b = wk.x;
-    kt = wk.y;
+    kw0 = wk.y * BNK + kwave * 32;
     qt_lo = wk.z;
     qt_hi = wk.w;
     bg = b * Hkv + (int)(blockIdx.x % Hkv);
+  } else if (CAUSAL && TEAMS == 1 && p.mirror) {
+    // mirrored key blocks (see mirror_block): the walk starts at the
+    // workgroup's first key
+    const int Lw = xcd_remap(blockIdx.x, p.B * Hkv * nkt);
+    bg = Lw / nkt;
+    const int l = Lw - bg * nkt;
+    kw0 = 32 * mirror_block(l, kwave, KW, nkt);
+    b = bg / Hkv;
+    qt_lo = 32 * l * (KW / 2) / BMQ;
+    qt_hi = (N - 1) / BMQ;
   } else {
     const int Lw = xcd_remap(blockIdx.x, p.B * Hkv * nkt);
     bg = Lw / nkt;
@@ -351,7 +366,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     // order: the two workgroups a CU receives pair a heavy tile with a light
     // one.  Teams fill a CU with one workgroup; heaviest first then.
     const int half = (nkt + 1) / 2;
-    kt = (TEAMS == 1 && G > 1 && l >= half) ? nkt - 1 - (l - half) : l;
+    const int kt = (TEAMS == 1 && G > 1 && l >= half) ? nkt - 1 - (l - half) : l;
+    kw0 = kt * BNK + kwave * 32;
     b = bg / Hkv;
     qt_lo = CAUSAL ? kt * BNK / BMQ : 0;
     qt_hi = (N - 1) / BMQ;
@@ -368,8 +384,6 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   const int nqs = (nq + QSUB - 1) / QSUB;
   const int nit = nq > 0 ? GT * nqs : 0;
 
-  const int k0 = kt * BNK;
-  const int kw0 = k0 + kwave * 32;
   const int kj = kw0 + col;
   const int kc_ = min(kj, N - 1);
   const int klast = min(kw0 + 31, N - 1);

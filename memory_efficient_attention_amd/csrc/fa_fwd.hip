@@ -57,20 +57,28 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
   // longest-first work list.  Dense: each XCD takes a contiguous range of
   // heads, the last (for causal, longest) query tiles first.
   const bool packed = p.seg != nullptr;
-  int bh, b, qt, kt_lo = 0, kt_hi;
+  // (mirrored blocks: see mirror_block)
+  int bh, b, kt_lo = 0, kt_hi, qw0;
   if (packed) {
     const int4 wk = p.work[blockIdx.x / p.H];
     b = wk.x;
-    qt = wk.y;
+    qw0 = wk.y * BM + wave * 32;
     kt_lo = wk.z;
     kt_hi = wk.w;
     bh = b * p.H + (int)(blockIdx.x % p.H);
   } else {
     const int Lw = xcd_remap(blockIdx.x, p.B * p.H * p.nqt);
     bh = Lw / p.nqt;
-    qt = p.nqt - 1 - (Lw - bh * p.nqt);
     b = bh / p.H;
-    kt_hi = ((CAUSAL ? min(qt * BM + BM, N) : N) - 1) / BN;
+    if (CAUSAL && p.mirror) {
+      const int t = Lw - bh * p.nqt;
+      qw0 = 32 * mirror_block(t, wave, NW, p.nqt);
+      kt_hi = (32 * (p.nqt * NW - t * (NW / 2)) - 1) / BN;
+    } else {
+      const int qt = p.nqt - 1 - (Lw - bh * p.nqt);
+      qw0 = qt * BM + wave * 32;
+      kt_hi = ((CAUSAL ? min(qt * BM + BM, N) : N) - 1) / BN;
+    }
   }
   // q and o rows of head bh; k and v of its key/value head (grouped-query
   // heads form contiguous runs of G)
@@ -82,8 +90,6 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
   const int32_t* seg = packed ? p.seg + (size_t)b * N : nullptr;
 
   // The wave owns queries qw0 .. qw0 + 31; lane l holds query qw0 + l % 32.
-  const int q0 = qt * BM;
-  const int qw0 = q0 + wave * 32;
   const int qi = qw0 + col;
   const int qc = min(qi, N - 1);
   const int qlast = min(qw0 + 31, N - 1);

@@ -115,6 +115,7 @@ struct FwdParams {
   const int4* work;
   int B, H, N, nqt;
   int G;                 // query heads per key/value head (H / Hkv)
+  int mirror;            // dense causal: mirrored 32-row blocks (mirror_block)
   float scale;           // softmax scale
   float c;               // scale * log2(e)
 };
@@ -136,8 +137,20 @@ struct BwdParams {
   const int4* work;
   int B, H, N, ntiles;
   int G;                 // query heads per key/value head (H / Hkv)
+  int mirror;            // dense causal: mirrored 32-row blocks (mirror_block)
   float scale, c;
 };
+
+// Causal grids of one or two rounds of the chip's CUs last as long as their
+// heaviest workgroups (last query tile, or first key tile).  There,
+// workgroup t of a head (of nt, nt * NW * 32 = N rows) gives its first NW / 2
+// waves the 32-row blocks t NW / 2 + w and the others the mirrored blocks
+// from the far end, so all workgroups carry the same visible work.  Every row
+// is still walked in the same order.
+__device__ __forceinline__ int mirror_block(int t, int w, int nw, int nt) {
+  const int half = nw / 2, x = t * half + w % half;
+  return w < half ? x : nt * nw - 1 - x;
+}
 
 struct PreParams {
   const void* o;

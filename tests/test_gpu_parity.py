@@ -54,8 +54,10 @@ def _compare(out, ref, dtype, sl=(slice(None),), tag=""):
 
 # ---------------------------------------------------------------- small shapes
 
+# N = 512 and 768 (whole 256-row workgroups, grids far below one per CU) take
+# the mirrored block order in dense causal calls
 SHAPES = [(1, 2, 1, 64), (1, 1, 17, 64), (2, 2, 255, 128), (1, 2, 257, 64), (1, 3, 300, 128),
-          (2, 1, 129, 128), (1, 2, 200, 96), (2, 1, 65, 96)]
+          (2, 1, 129, 128), (1, 2, 200, 96), (2, 1, 65, 96), (1, 2, 512, 64), (2, 3, 768, 128)]
 MODES = {"causal": (False, True), "packed": (True, True), "packed_bidir": (True, False),
          "full": (False, False)}
 
@@ -78,7 +80,7 @@ def test_small_shapes(B, H, N, D, dtype, mode):
 # group sizes 2 and 4 take the two-team dK/dV workgroups in dense bf16 calls;
 # the group of 3 takes the single-team one
 GQA_SHAPES = [(1, 4, 2, 129, 64), (2, 4, 1, 257, 128), (1, 6, 3, 200, 128), (1, 4, 2, 150, 96),
-              (1, 6, 2, 160, 128)]
+              (1, 6, 2, 160, 128), (1, 4, 2, 512, 128)]
 
 
 @pytest.mark.parametrize("mode", list(MODES))
@@ -269,6 +271,21 @@ def test_single_segment_8k_bitwise_equals_causal():
     o_r, l_r = attention_rows(t["q"][0, 3], t["k"][0, 3], t["v"][0, 3], rows, None, w.scale, True)
     check_o(down(packed["o"][0, 3, rows]), o_r, w.dtype)
     check_lse(down(packed["lse"][0, 3, rows]), l_r, w.dtype)
+
+
+@pytest.mark.parametrize("H,N", [(32, 2048), (32, 4096)])
+def test_single_segment_bitwise_equals_causal_mirrored(H, N):
+    """Dense causal grids of one (2k) or two (4k) rounds of the chip's CUs
+    take the mirrored block order; the packed path never does.  Both must
+    agree to the bit, since every row is walked in the same order."""
+    w = workloads.get("causal_2k").with_(H=H, N=N)
+    say(f"B1 H{H} N{N} D128 bf16 as one segment and as plain causal")
+    t = w.tensors()
+    seg = np.zeros((w.B, w.N), dtype=np.int32)
+    packed = run_gpu(t, seg, w.dtype, w.scale, True)
+    causal = run_gpu(t, None, w.dtype, w.scale, True)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert bool((packed[n] == causal[n]).all()), f"{n}: single-segment packed != causal"
 
 
 def test_packed_long_documents_64k():
