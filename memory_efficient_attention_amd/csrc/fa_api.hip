@@ -106,11 +106,14 @@ int device_cus() {
 
 // Mirrored 32-row blocks (mirror_block in the kernels) for a dense causal
 // launch of `wgs` workgroups of `nw` waves over N rows, when the blocks tile
-// N exactly and the grid needs at most two rounds of the chip's CUs.  Up to
-// there the heaviest workgroups set the step time; on larger grids the
+// N exactly: the number of rounds of the chip's CUs the grid needs (1 or 2),
+// else 0.  Up to two rounds the heaviest workgroups set the step time (the
+// two-team dK/dV kernel gains at one round only); on larger grids the
 // heaviest-first order packs unequal workgroups as well or better.
 int use_mirror(bool dense, int causal, int N, int nw, long long wgs) {
-  return dense && causal && N % (nw * 32) == 0 && wgs <= 2LL * device_cus() ? 1 : 0;
+  const long long cus = device_cus();
+  if (!dense || !causal || N % (nw * 32) != 0 || cus <= 0 || wgs > 2 * cus) return 0;
+  return wgs <= cus ? 1 : 2;
 }
 
 fa_status common_checks(int B, int H, int Hkv, int N, int D, fa_dtype dtype, float scale) {
@@ -257,8 +260,8 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   if (!record(events, 1, s)) return FA_ERR_HIP;
   p.work = seg ? (const int4*)(w + L.kwork) : nullptr;
   p.ntiles = ntiles_kv;
-  // key blocks mirror in the one-team kernel of ungrouped heads only
-  p.mirror = use_mirror(seg == nullptr && Hkv == H, causal, N, nw_kv, (long long)B * Hkv * ntiles_kv);
+  // (the kernel applies it to ungrouped heads and two-team workgroups)
+  p.mirror = use_mirror(seg == nullptr, causal, N, nw_kv, (long long)B * Hkv * ntiles_kv);
   if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, nw_kv, s) != hipSuccess) return FA_ERR_HIP;
 
   if (!record(events, 2, s)) return FA_ERR_HIP;

@@ -308,7 +308,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   constexpr int PER_STAGE = TEAMS * (2 * TILE + 2 * VEC) + VEC;
   constexpr int S = sizeof(T) == 2 ? stages_for(FA_DKV_STAGES, PER_STAGE, NW) : 2;
   static_assert(S >= 2 && S * PER_STAGE <= LDS_PER_CU, "Q/dO stages must fit in LDS");
-  static_assert(TEAMS == 1 || (TEAMS == 2 && sizeof(T) == 2), "teams: bf16 only");
+  static_assert(TEAMS == 1 || (TEAMS == 2 && sizeof(T) == 2 && NW == 8), "teams: bf16, 8 waves");
   static_assert(TEAMS == 1 || S * PER_STAGE >= KW * 32 * D * 4, "team reduction reuses the ring");
   // The 2 TEAMS Q and dO tiles of a stage share one stager's per-lane
   // offsets when one tile's instructions already reach every wave; otherwise
@@ -324,8 +324,11 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int team = TEAMS == 1 ? 0 : wave / KW;
-  const int kwave = TEAMS == 1 ? wave : wave % KW;
+  // Teams: waves {0, 1, 4, 5} form team 0 and {2, 3, 6, 7} team 1, so that
+  // each SIMD (waves w and w + 4) holds key waves kw and kw + 2 of one team.
+  // With mirrored key blocks those are one early and one late block.
+  const int team = TEAMS == 1 ? 0 : (wave >> 1) & 1;
+  const int kwave = TEAMS == 1 ? wave : (wave & 1) | ((wave >> 2) << 1);
   const int h = lane >> 5, col = lane & 31;
   const int N = p.N;
   const int nkt = p.ntiles;
@@ -346,9 +349,12 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     qt_lo = wk.z;
     qt_hi = wk.w;
     bg = b * Hkv + (int)(blockIdx.x % Hkv);
-  } else if (CAUSAL && TEAMS == 1 && p.mirror) {
-    // mirrored key blocks (see mirror_block): the walk starts at the
-    // workgroup's first key
+  } else if (CAUSAL && (TEAMS == 2 ? p.mirror == 1 : G == 1 && p.mirror != 0)) {
+    // mirrored key blocks (see mirror_block) over the key waves, the same in
+    // both teams (one round of workgroups only: at two, the heaviest-first
+    // order already pairs heavy and light teams); the walk starts at the
+    // workgroup's first key.  The one-team kernel of grouped heads keeps its
+    // own heavy/light pairing.
     const int Lw = xcd_remap(blockIdx.x, p.B * Hkv * nkt);
     bg = Lw / nkt;
     const int l = Lw - bg * nkt;

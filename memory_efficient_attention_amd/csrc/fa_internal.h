@@ -116,6 +116,7 @@ struct FwdParams {
   int B, H, N, nqt;
   int G;                 // query heads per key/value head (H / Hkv)
   int mirror;            // dense causal: mirrored 32-row blocks (mirror_block)
+                         // when nonzero; the grid's rounds of CUs (1 or 2)
   float scale;           // softmax scale
   float c;               // scale * log2(e)
 };
@@ -137,7 +138,7 @@ struct BwdParams {
   const int4* work;
   int B, H, N, ntiles;
   int G;                 // query heads per key/value head (H / Hkv)
-  int mirror;            // dense causal: mirrored 32-row blocks (mirror_block)
+  int mirror;            // as in FwdParams
   float scale, c;
 };
 
