@@ -57,7 +57,8 @@ def _compare(out, ref, dtype, sl=(slice(None),), tag=""):
 # N = 512 and 768 (whole 256-row workgroups, grids far below one per CU) take
 # the mirrored block order in dense causal calls
 SHAPES = [(1, 2, 1, 64), (1, 1, 17, 64), (2, 2, 255, 128), (1, 2, 257, 64), (1, 3, 300, 128),
-          (2, 1, 129, 128), (1, 2, 200, 96), (2, 1, 65, 96), (1, 2, 512, 64), (2, 3, 768, 128)]
+          (2, 1, 129, 128), (1, 2, 200, 96), (2, 1, 65, 96), (1, 2, 512, 64), (2, 3, 768, 128),
+          (1, 2, 512, 96)]
 MODES = {"causal": (False, True), "packed": (True, True), "packed_bidir": (True, False),
          "full": (False, False)}
 
@@ -78,9 +79,10 @@ def test_small_shapes(B, H, N, D, dtype, mode):
 
 
 # group sizes 2 and 4 take the two-team dK/dV workgroups in dense bf16 calls;
-# the group of 3 takes the single-team one
+# the group of 3 takes the single-team one.  N a multiple of 128 (256 for
+# the forward and dQ) takes the mirrored block order in dense causal calls.
 GQA_SHAPES = [(1, 4, 2, 129, 64), (2, 4, 1, 257, 128), (1, 6, 3, 200, 128), (1, 4, 2, 150, 96),
-              (1, 6, 2, 160, 128), (1, 4, 2, 512, 128)]
+              (1, 6, 2, 160, 128), (1, 4, 2, 512, 128), (1, 4, 2, 384, 64), (1, 6, 3, 256, 128)]
 
 
 @pytest.mark.parametrize("mode", list(MODES))
