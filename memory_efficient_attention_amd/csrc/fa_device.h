@@ -254,19 +254,6 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
   wait_vm<0>();
 }
 
-// Optional wave priority around MFMA issue phases (build with -DFA_SETPRIO=1):
-// a wave issuing a block of MFMAs is preferred by the SIMD's arbiter over its
-// co-resident wave, which is then left the VALU.
-#ifndef FA_SETPRIO
-#define FA_SETPRIO 0
-#endif
-__device__ __forceinline__ void prio_hi() {
-  if (FA_SETPRIO) __builtin_amdgcn_s_setprio(1);
-}
-__device__ __forceinline__ void prio_lo() {
-  if (FA_SETPRIO) __builtin_amdgcn_s_setprio(0);
-}
-
 // A/B fragment along D: 8 consecutive elements of tile row rb + lane % 32 at
 // column 8 * (2 * ks + lane / 32); rb is a multiple of 4, `base` =
 // Layout::row_base(lane).
