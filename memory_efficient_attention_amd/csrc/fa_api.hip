@@ -105,13 +105,13 @@ int device_cus() {
 }
 
 // Mirrored 32-row blocks (mirror_block in the kernels) for a dense causal
-// launch of `wgs` workgroups of `nw` waves over N rows, when the blocks tile
-// N exactly: the number of rounds of the chip's CUs the grid needs (1 or 2),
-// else 0.  Up to two rounds the heaviest workgroups set the step time (the
-// two-team dK/dV kernel gains at one round only); on larger grids the
-// heaviest-first order packs unequal workgroups as well or better.
-int use_mirror(bool dense, int causal, int N, int nw, long long wgs) {
-  const long long cus = device_cus();
+// launch of `wgs` workgroups of `nw` waves over N rows on a device of `cus`
+// compute units, when the blocks tile N exactly: the number of rounds of the
+// CUs the grid needs (1 or 2), else 0.  Up to two rounds the heaviest
+// workgroups set the step time (the two-team dK/dV kernel gains at one round
+// only); on larger grids the heaviest-first order packs unequal workgroups as
+// well or better.
+int use_mirror(bool dense, int causal, int N, int nw, long long wgs, long long cus) {
   if (!dense || !causal || N % (nw * 32) != 0 || cus <= 0 || wgs > 2 * cus) return 0;
   return wgs <= cus ? 1 : 2;
 }
@@ -169,7 +169,7 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   const int nw = fa::tile_config(seg != nullptr, Hkv != H).nw_q;
   const int bm = nw * 32;   // queries per workgroup
   p.nqt = (N + bm - 1) / bm;
-  p.mirror = use_mirror(seg == nullptr, causal, N, nw, (long long)B * H * p.nqt);
+  p.mirror = use_mirror(seg == nullptr, causal, N, nw, (long long)B * H * p.nqt, device_cus());
   p.scale = scale;
   p.c = log2e_scale(scale);
   if (seg) {
@@ -256,18 +256,19 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   p.N = N;
   p.scale = scale;
   p.c = log2e_scale(scale);
+  const int cus = device_cus();
 
   if (!record(events, 1, s)) return FA_ERR_HIP;
   p.work = seg ? (const int4*)(w + L.kwork) : nullptr;
   p.ntiles = ntiles_kv;
   // (the kernel applies it to ungrouped heads and two-team workgroups)
-  p.mirror = use_mirror(seg == nullptr, causal, N, nw_kv, (long long)B * Hkv * ntiles_kv);
+  p.mirror = use_mirror(seg == nullptr, causal, N, nw_kv, (long long)B * Hkv * ntiles_kv, cus);
   if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, nw_kv, s) != hipSuccess) return FA_ERR_HIP;
 
   if (!record(events, 2, s)) return FA_ERR_HIP;
   p.work = seg ? (const int4*)(w + L.qwork) : nullptr;
   p.ntiles = ntiles;
-  p.mirror = use_mirror(seg == nullptr, causal, N, nw, (long long)B * H * ntiles);
+  p.mirror = use_mirror(seg == nullptr, causal, N, nw, (long long)B * H * ntiles, cus);
   if (fa::launch_bwd_dq(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
   if (!record(events, 3, s)) return FA_ERR_HIP;
   return FA_OK;
