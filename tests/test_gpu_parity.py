@@ -156,6 +156,35 @@ def test_rising_and_falling_scores(D, dtype):
             check_grad(down(out[n]), ref[n], dtype, n)
 
 
+def _sweep_cases(n=32, seed=4242):
+    """A fixed, seeded list of small mixed configurations: batch, heads,
+    group size, odd and whole-tile lengths, every head dim, both dtypes and
+    every masking mode, with segment lengths from 1 token to the whole row."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 2, 3, 4]))
+        N = int(rng.choice([int(rng.integers(1, 600)), 128 * int(rng.integers(1, 5))]))
+        cases.append(dict(B=int(rng.integers(1, 3)), H=Hkv * G, Hkv=Hkv, N=N, D=int(rng.choice([64, 96, 128])),
+                          dtype=str(rng.choice(["bf16", "fp32"])), mode=str(rng.choice(list(MODES))),
+                          max_len=int(rng.choice([1, 7, 60, N])), seed=5000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "B{B}H{H}Hkv{Hkv}N{N}D{D}{dtype}{mode}L{max_len}".format(**c))
+def test_seeded_sweep(case):
+    """Mixed small configurations against the full oracle."""
+    c = case
+    packed, causal = MODES[c["mode"]]
+    say(f"sweep {c}")
+    t = workloads.make_tensors(c["B"], c["H"], c["N"], c["D"], c["dtype"], c["seed"], Hkv=c["Hkv"])
+    seg = workloads.random_segments(c["B"], c["N"], c["seed"], max_len=c["max_len"]) if packed else None
+    scale = 1.0 / np.sqrt(c["D"])
+    out = run_gpu(t, seg, c["dtype"], scale, causal)
+    _compare(out, _oracle_full(t, seg, scale, causal), c["dtype"])
+
+
 # ---------------------------------------------------------------- the workloads
 
 def test_tiny_fp32_one_segment():
