@@ -113,14 +113,29 @@ def test_short_segments_many_tiles():
         _compare(out, _oracle_full(t, seg, 0.09, causal), "bf16")
 
 
-def test_segment_ids_need_not_start_at_zero():
-    """Ids are compared for equality only; any non-decreasing ids work."""
+@pytest.mark.parametrize("offset", [1000, -5000])
+def test_segment_ids_need_not_start_at_zero(offset):
+    """Ids are compared for equality and order only; any non-decreasing ids
+    work, negative ones included."""
     B, H, N, D = 1, 2, 200, 64
-    say("offset segment ids B1 H2 N200 D64")
+    say(f"offset segment ids B1 H2 N200 D64, offset {offset}")
     t = workloads.make_tensors(B, H, N, D, "bf16", 78)
-    seg = workloads.random_segments(B, N, 78, max_len=50) * 3 + 1000
+    seg = workloads.random_segments(B, N, 78, max_len=50) * 3 + offset
     out = run_gpu(t, seg, "bf16", 0.125, True)
     _compare(out, _oracle_full(t, seg, 0.125, True), "bf16")
+
+
+@pytest.mark.parametrize("mode", ["causal", "packed"])
+def test_many_short_sequences(mode):
+    """A large batch of short rows: thousands of one-tile workgroups, each
+    row's tail inside its only tile."""
+    B, H, N, D = 48, 8, 45, 64
+    packed, causal = MODES[mode]
+    say(f"many short rows B{B} H{H} N{N} D{D} bf16 {mode}")
+    t = workloads.make_tensors(B, H, N, D, "bf16", 80)
+    seg = workloads.random_segments(B, N, 80, max_len=12) if packed else None
+    out = run_gpu(t, seg, "bf16", 0.125, causal)
+    _compare(out, _oracle_full(t, seg, 0.125, causal), "bf16")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
