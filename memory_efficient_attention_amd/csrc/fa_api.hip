@@ -173,10 +173,11 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   p.scale = scale;
   p.c = log2e_scale(scale);
   if (seg) {
-    if (fa::launch_qtile_table(seg, B, N, bm, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
-            hipSuccess ||
-        fa::launch_tile_order((const int2*)(w + L.qtab), B, p.nqt, (int4*)(w + L.qwork), seg, N,
-                              (int32_t*)(w + L.flag), s) != hipSuccess)
+    fa::TableJobs tj{};
+    fa::OrderJobs oj{};
+    tj.j[0] = {(int2*)(w + L.qtab), bm, fa::KEY_TILE, 0};
+    oj.j[0] = {(const int2*)(w + L.qtab), p.nqt, (int4*)(w + L.qwork), 1};
+    if (fa::launch_schedule(seg, B, N, causal != 0, tj, oj, 1, (int32_t*)(w + L.flag), s) != hipSuccess)
       return FA_ERR_HIP;
   }
   if (fa::launch_fwd(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
@@ -217,14 +218,14 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   const int ntiles = (N + bt - 1) / bt;
   const int ntiles_kv = (N + nw_kv * 32 - 1) / (nw_kv * 32);
   if (seg) {
-    if (fa::launch_qtile_table(seg, B, N, bt, fa::KEY_TILE, causal != 0, (int2*)(w + L.qtab), s) !=
-            hipSuccess ||
-        fa::launch_ktile_table(seg, B, N, nw_kv * 32, fa::QRY_TILE, causal != 0, (int2*)(w + L.ktab), s) !=
-            hipSuccess ||
-        fa::launch_tile_order((const int2*)(w + L.qtab), B, ntiles, (int4*)(w + L.qwork), seg, N,
-                              (int32_t*)(w + L.flag), s) != hipSuccess ||
-        fa::launch_tile_order((const int2*)(w + L.ktab), B, ntiles_kv, (int4*)(w + L.kwork), nullptr, N,
-                              nullptr, s) != hipSuccess)
+    // query tiles of dQ (and the segment-order check), key tiles of dK/dV
+    fa::TableJobs tj{};
+    fa::OrderJobs oj{};
+    tj.j[0] = {(int2*)(w + L.qtab), bt, fa::KEY_TILE, 0};
+    tj.j[1] = {(int2*)(w + L.ktab), nw_kv * 32, fa::QRY_TILE, 1};
+    oj.j[0] = {(const int2*)(w + L.qtab), ntiles, (int4*)(w + L.qwork), 1};
+    oj.j[1] = {(const int2*)(w + L.ktab), ntiles_kv, (int4*)(w + L.kwork), 0};
+    if (fa::launch_schedule(seg, B, N, causal != 0, tj, oj, 2, (int32_t*)(w + L.flag), s) != hipSuccess)
       return FA_ERR_HIP;
   }
 

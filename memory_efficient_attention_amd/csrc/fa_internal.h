@@ -209,14 +209,28 @@ hipError_t dispatch(int dtype, int D, bool causal, int nw, F&& f) {
   };
   return dtype == 0 ? by_d(type_c<__bf16>{}) : by_d(type_c<float>{});
 }
-// Per-tile range tables from segment ids (see fa_sched.hip).
-hipError_t launch_qtile_table(const int32_t* seg, int B, int N, int tq, int tk, bool causal,
-                              int2* tab, hipStream_t s);
-hipError_t launch_ktile_table(const int32_t* seg, int B, int N, int tk, int tq, bool causal,
-                              int2* tab, hipStream_t s);
-// Longest-first work list {b, tile, first, last} from a range table of B x nt
-// tiles (and, with check_seg, the segment-order check into flag).
-hipError_t launch_tile_order(const int2* tab, int B, int nt, int4* work, const int32_t* check_seg, int N,
-                             int32_t* flag, hipStream_t s);
+// Packed-row schedule (fa_sched.hip): for one or two jobs in one pair of
+// launches, per-tile visible ranges from segment ids, then a longest-first
+// work list {b, tile, first, last} per table.
+struct TableJob {
+  int2* tab;     // out: B x ceil(N / tile) {first, last}
+  int tile;      // rows per tile of this table (queries, or keys if `keys`)
+  int other;     // rows per tile of the ranges (keys, or queries if `keys`)
+  int keys;      // 0: query tiles -> key-tile ranges; 1: key tiles -> query-tile ranges
+};
+struct OrderJob {
+  const int2* tab;   // a table of B x nt tiles
+  int nt;
+  int4* work;        // out: B x nt entries, longest range first
+  int check;         // also raise flag[0] if a row's ids decrease (one job at most)
+};
+struct TableJobs {
+  TableJob j[2];
+};
+struct OrderJobs {
+  OrderJob j[2];
+};
+hipError_t launch_schedule(const int32_t* seg, int B, int N, bool causal, const TableJobs& tables,
+                           const OrderJobs& orders, int njobs, int32_t* flag, hipStream_t s);
 
 }  // namespace fa

@@ -42,73 +42,82 @@ __device__ __forceinline__ int first_above(const int32_t* s, int n, int v) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// For each query tile of tq rows: the first and last key tile (of tk keys)
-// holding a key some query of the tile can see.
-__global__ void __launch_bounds__(256) qtile_table_kernel(const int32_t* seg, int B, int N, int tq,
-                                                          int tk, int causal, int2* tab) {
-  const int ntiles = (N + tq - 1) / tq;
+// Per-tile visible ranges, for one or two tables in one launch (blockIdx.y
+// selects the job).  A query-tile job (keys = 0) gives, for each tile of
+// `tile` queries, the first and last tile of `other` keys holding a key some
+// query of the tile can see; a key-tile job (keys = 1) gives, for each tile of
+// `tile` keys, the first and last tile of `other` queries holding a query that
+// can see some key of the tile.
+__global__ void __launch_bounds__(256) table_kernel(const int32_t* seg, int B, int N, int causal,
+                                                    TableJobs jobs) {
+  const TableJob J = jobs.j[blockIdx.y];
+  const int ntiles = (N + J.tile - 1) / J.tile;
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   if (t >= (long long)B * ntiles) return;
-  const int b = (int)(t / ntiles), qt = (int)(t % ntiles);
+  const int b = (int)(t / ntiles), it = (int)(t % ntiles);
   const int32_t* s = seg + (size_t)b * N;
-  const int q0 = qt * tq, q1 = min(q0 + tq, N) - 1;
-  int lo = first_at_least(s, N, s[q0]);
-  int hi = causal ? q1 : first_above(s, N, s[q1]) - 1;
+  const int r0 = it * J.tile, r1 = min(r0 + J.tile, N) - 1;
+  int lo, hi;
+  if (J.keys) {
+    lo = causal ? r0 : first_at_least(s, N, s[r0]);
+    hi = first_above(s, N, s[r1]) - 1;
+  } else {
+    lo = first_at_least(s, N, s[r0]);
+    hi = causal ? r1 : first_above(s, N, s[r1]) - 1;
+  }
   lo = clampi(lo, 0, N - 1);
   hi = clampi(hi, 0, N - 1);
-  tab[t] = make_int2(lo / tk, hi / tk);
-}
-
-// For each key tile of tk keys: the first and last query tile (of tq rows)
-// holding a query that can see some key of the tile.
-__global__ void __launch_bounds__(256) ktile_table_kernel(const int32_t* seg, int B, int N, int tk,
-                                                          int tq, int causal, int2* tab) {
-  const int ntiles = (N + tk - 1) / tk;
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (long long)B * ntiles) return;
-  const int b = (int)(t / ntiles), kt = (int)(t % ntiles);
-  const int32_t* s = seg + (size_t)b * N;
-  const int k0 = kt * tk, k1 = min(k0 + tk, N) - 1;
-  int lo = causal ? k0 : first_at_least(s, N, s[k0]);
-  int hi = first_above(s, N, s[k1]) - 1;
-  lo = clampi(lo, 0, N - 1);
-  hi = clampi(hi, 0, N - 1);
-  tab[t] = make_int2(lo / tq, hi / tq);
+  J.tab[t] = make_int2(lo / J.other, hi / J.other);
 }
 
 // Longest-first work list from a range table of n = B * nt tiles: work[k] =
 // {b, tile, first, last} with k ordered by descending range length (clamped
 // to 255 tiles), by a counting sort in LDS.  Ties come out in any order; the
 // order only decides which workgroup starts first, never what a workgroup
-// computes.  With seg given, also flag[0] = 1 if some row's ids decrease,
-// else 0.  One workgroup.
-__global__ void __launch_bounds__(1024) order_kernel(const int2* tab, int n, int nt, int4* work,
-                                                     const int32_t* seg, int B, int N, int32_t* flag) {
+// computes.  A job with `check` set also writes flag[0] = 1 if some row's
+// ids decrease, else 0.  One workgroup per job.
+__global__ void __launch_bounds__(1024) order_kernel(const int32_t* seg, int B, int N, int32_t* flag,
+                                                     OrderJobs jobs) {
   constexpr int NB = 256;
   __shared__ int cnt[NB];
+  __shared__ int wsum[NB / 64];
+  const OrderJob J = jobs.j[blockIdx.x];
+  const int n = B * J.nt;
   const int tid = threadIdx.x;
   for (int i = tid; i < NB; i += 1024) cnt[i] = 0;
   __syncthreads();
   auto bucket = [&](int i) {
-    const int2 r = tab[i];
+    const int2 r = J.tab[i];
     return NB - 1 - clampi(r.y - r.x + 1, 0, NB - 1);   // longest first
   };
   for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[bucket(i)], 1);
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int k = 0; k < NB; ++k) {
-      const int c = cnt[k];
-      cnt[k] = acc;
-      acc += c;
+  // exclusive prefix sum of the bucket counts: a shuffle scan within each of
+  // the first NB / 64 waves, then the preceding waves' totals
+  int own = 0, incl = 0;
+  if (tid < NB) {
+    own = cnt[tid];
+    incl = own;
+    const int lane = tid & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
     }
+    if (lane == 63) wsum[tid >> 6] = incl;
+  }
+  __syncthreads();
+  if (tid < NB) {
+    int base = 0;
+    for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
+    cnt[tid] = base + incl - own;
   }
   __syncthreads();
   for (int i = tid; i < n; i += 1024) {
-    const int2 r = tab[i];
-    work[atomicAdd(&cnt[bucket(i)], 1)] = make_int4(i / nt, i % nt, r.x, r.y);
+    const int2 r = J.tab[i];
+    J.work[atomicAdd(&cnt[bucket(i)], 1)] = make_int4(i / J.nt, i % J.nt, r.x, r.y);
   }
-  if (seg) {
+  if (J.check) {
     int bad = 0;
     const long long m = (long long)B * N;
     for (long long i = tid; i < m; i += 1024) {
@@ -119,25 +128,17 @@ __global__ void __launch_bounds__(1024) order_kernel(const int2* tab, int n, int
   }
 }
 
-hipError_t launch_qtile_table(const int32_t* seg, int B, int N, int tq, int tk, bool causal,
-                              int2* tab, hipStream_t s) {
-  const long long n = (long long)B * ((N + tq - 1) / tq);
-  hipLaunchKernelGGL(qtile_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, seg, B, N,
-                     tq, tk, causal ? 1 : 0, tab);
-  return hipGetLastError();
-}
-
-hipError_t launch_ktile_table(const int32_t* seg, int B, int N, int tk, int tq, bool causal,
-                              int2* tab, hipStream_t s) {
-  const long long n = (long long)B * ((N + tk - 1) / tk);
-  hipLaunchKernelGGL(ktile_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, seg, B, N,
-                     tk, tq, causal ? 1 : 0, tab);
-  return hipGetLastError();
-}
-
-hipError_t launch_tile_order(const int2* tab, int B, int nt, int4* work, const int32_t* check_seg, int N,
-                             int32_t* flag, hipStream_t s) {
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s, tab, B * nt, nt, work, check_seg, B, N, flag);
+hipError_t launch_schedule(const int32_t* seg, int B, int N, bool causal, const TableJobs& tables,
+                           const OrderJobs& orders, int njobs, int32_t* flag, hipStream_t s) {
+  long long n = 0;
+  for (int j = 0; j < njobs; ++j) {
+    const long long nj = (long long)B * ((N + tables.j[j].tile - 1) / tables.j[j].tile);
+    n = nj > n ? nj : n;
+  }
+  hipLaunchKernelGGL(table_kernel, dim3((unsigned)((n + 255) / 256), (unsigned)njobs), dim3(256), 0, s, seg,
+                     B, N, causal ? 1 : 0, tables);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(order_kernel, dim3((unsigned)njobs), dim3(1024), 0, s, seg, B, N, flag, orders);
   return hipGetLastError();
 }
 
