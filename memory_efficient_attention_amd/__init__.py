@@ -110,9 +110,11 @@ def _dtype_code(t) -> int:
     return 99   # the library refuses it with FA_ERR_DTYPE
 
 
-def _check_tensor(name, t, shape, dtype):
+def _check_tensor(name, t, shape, dtype, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if tuple(t.shape) != tuple(shape):
@@ -121,17 +123,47 @@ def _check_tensor(name, t, shape, dtype):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
-def _seg_ptr(seg, B, N):
+def _seg_ptr(seg, B, N, device):
     import torch
     if seg is None:
         return None
-    _check_tensor("seg", seg, (B, N), torch.int32)
+    _check_tensor("seg", seg, (B, N), torch.int32, device)
     return seg.data_ptr()
 
 
 def _stream():
+    """The current stream of the current device (calls run under the device
+    of their tensors, see _on)."""
     import torch
     return torch.cuda.current_stream().cuda_stream
+
+
+def _on(device):
+    """Make the tensors' device current for the library call, so that the
+    kernels and the stream are that device's."""
+    import torch
+    return torch.cuda.device(device)
+
+
+def _workspace(ws, nbytes, device, min_bytes=0):
+    """The caller's workspace, checked (device, layout, size: a caller that
+    passes one gets no allocation), or a new one of max(nbytes, min_bytes)
+    bytes (None when the call needs none).  Returns (tensor or None, its size
+    in bytes)."""
+    import torch
+    if ws is None:
+        if nbytes == 0 and min_bytes == 0:
+            return None, 0
+        ws = torch.empty(max(nbytes, min_bytes), dtype=torch.uint8, device=device)
+        return ws, ws.numel()
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    size = ws.numel() * ws.element_size()
+    if size < nbytes:
+        raise ValueError(f"workspace has {size} bytes, {nbytes} needed")
+    return ws, size
 
 
 def _kv_heads(q, k) -> int:
@@ -148,24 +180,23 @@ def fa_fwd(q, k, v, seg=None, scale=None, causal=True, out=None, lse=None, works
     import torch
     B, H, N, D = q.shape
     Hkv = _kv_heads(q, k)
+    dev = q.device
     _check_tensor("q", q, (B, H, N, D), q.dtype)
     for name, t in (("k", k), ("v", v)):
-        _check_tensor(name, t, (B, Hkv, N, D), q.dtype)
+        _check_tensor(name, t, (B, Hkv, N, D), q.dtype, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_tensor("o", o, (B, H, N, D), q.dtype)
-    _check_tensor("lse", lse_t, (B, H, N), torch.float32)
-    seg_p = _seg_ptr(seg, B, N)
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check_tensor("o", o, (B, H, N, D), q.dtype, dev)
+    _check_tensor("lse", lse_t, (B, H, N), torch.float32, dev)
+    seg_p = _seg_ptr(seg, B, N, dev)
     lib = load_library()
     nbytes = lib.fa_workspace_bytes(B, H, N, D, int(seg is not None), 0)
-    ws = workspace
-    if nbytes and (ws is None or ws.numel() < nbytes):
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_p, ctypes.c_float(scale),
-                    int(bool(causal)), o.data_ptr(), lse_t.data_ptr(), B, H, Hkv, N, D,
-                    _dtype_code(q), ws.data_ptr() if (ws is not None and nbytes) else None,
-                    nbytes, _stream())
+    ws, ws_bytes = _workspace(workspace, nbytes, dev)
+    with _on(dev):
+        st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_p, ctypes.c_float(scale),
+                        int(bool(causal)), o.data_ptr(), lse_t.data_ptr(), B, H, Hkv, N, D,
+                        _dtype_code(q), ws.data_ptr() if ws is not None else None, ws_bytes, _stream())
     if st:
         raise FaError(st, "fa_fwd")
     return o, lse_t
@@ -180,33 +211,33 @@ def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=N
     import torch
     B, H, N, D = q.shape
     Hkv = _kv_heads(q, k)
+    dev = q.device
     for name, t in (("q", q), ("o", o), ("do", do)):
-        _check_tensor(name, t, (B, H, N, D), q.dtype)
+        _check_tensor(name, t, (B, H, N, D), q.dtype, dev)
     for name, t in (("k", k), ("v", v)):
-        _check_tensor(name, t, (B, Hkv, N, D), q.dtype)
-    _check_tensor("lse", lse, (B, H, N), torch.float32)
+        _check_tensor(name, t, (B, Hkv, N, D), q.dtype, dev)
+    _check_tensor("lse", lse, (B, H, N), torch.float32, dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _check_tensor("dq", dq, (B, H, N, D), q.dtype)
+    _check_tensor("dq", dq, (B, H, N, D), q.dtype, dev)
     for name, t in (("dk", dk), ("dv", dv)):
-        _check_tensor(name, t, (B, Hkv, N, D), q.dtype)
-    seg_p = _seg_ptr(seg, B, N)
+        _check_tensor(name, t, (B, Hkv, N, D), q.dtype, dev)
+    seg_p = _seg_ptr(seg, B, N, dev)
     lib = load_library()
     nbytes = lib.fa_workspace_bytes(B, H, N, D, int(seg is not None), 1)
-    ws = workspace
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-            lse.data_ptr(), seg_p, ctypes.c_float(scale), int(bool(causal)),
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, D, _dtype_code(q),
-            ws.data_ptr(), nbytes, _stream())
-    if events is None:
-        st = lib.fa_bwd(*args)
-    else:
-        ev = (ctypes.c_void_p * 4)(*[e or None for e in events])
-        st = lib.fa_bwd_timed(*args, ev)
+    ws, ws_bytes = _workspace(workspace, nbytes, dev)
+    with _on(dev):
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                lse.data_ptr(), seg_p, ctypes.c_float(scale), int(bool(causal)),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, D, _dtype_code(q),
+                ws.data_ptr(), ws_bytes, _stream())
+        if events is None:
+            st = lib.fa_bwd(*args)
+        else:
+            ev = (ctypes.c_void_p * 4)(*[e or None for e in events])
+            st = lib.fa_bwd_timed(*args, ev)
     if st:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
@@ -243,17 +274,17 @@ def fa_lce_fwd(h, w, targets, workspace=None):
     import torch
     N, D = h.shape
     V = w.shape[0]
+    dev = h.device
     _check_tensor("h", h, (N, D), h.dtype)
-    _check_tensor("w", w, (V, D), h.dtype)
-    _check_tensor("targets", targets, (N,), torch.int32)
-    nll, lse, tz = (torch.empty(N, dtype=torch.float32, device=h.device) for _ in range(3))
+    _check_tensor("w", w, (V, D), h.dtype, dev)
+    _check_tensor("targets", targets, (N,), torch.int32, dev)
+    nll, lse, tz = (torch.empty(N, dtype=torch.float32, device=dev) for _ in range(3))
     lib = load_library()
     nbytes = lib.fa_lce_workspace_bytes(N, V, D, 0)
-    ws = workspace
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=h.device)
-    st = lib.fa_lce_fwd(h.data_ptr(), w.data_ptr(), targets.data_ptr(), nll.data_ptr(), lse.data_ptr(),
-                        tz.data_ptr(), N, V, D, _dtype_code(h), ws.data_ptr(), ws.numel(), _stream())
+    ws, ws_bytes = _workspace(workspace, nbytes, dev, 256)
+    with _on(dev):
+        st = lib.fa_lce_fwd(h.data_ptr(), w.data_ptr(), targets.data_ptr(), nll.data_ptr(), lse.data_ptr(),
+                            tz.data_ptr(), N, V, D, _dtype_code(h), ws.data_ptr(), ws_bytes, _stream())
     if st:
         raise FaError(st, "fa_lce_fwd")
     return nll, lse, tz
@@ -265,21 +296,21 @@ def fa_lce_bwd(h, w, targets, lse, dnll, need_dw=True, workspace=None):
     import torch
     N, D = h.shape
     V = w.shape[0]
+    dev = h.device
     _check_tensor("h", h, (N, D), h.dtype)
-    _check_tensor("w", w, (V, D), h.dtype)
-    _check_tensor("targets", targets, (N,), torch.int32)
-    _check_tensor("lse", lse, (N,), torch.float32)
-    _check_tensor("dnll", dnll, (N,), torch.float32)
+    _check_tensor("w", w, (V, D), h.dtype, dev)
+    _check_tensor("targets", targets, (N,), torch.int32, dev)
+    _check_tensor("lse", lse, (N,), torch.float32, dev)
+    _check_tensor("dnll", dnll, (N,), torch.float32, dev)
     dh = torch.empty_like(h)
     dw = torch.empty_like(w) if need_dw else None
     lib = load_library()
     nbytes = lib.fa_lce_workspace_bytes(N, V, D, 1)
-    ws = workspace
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=h.device)
-    st = lib.fa_lce_bwd(h.data_ptr(), w.data_ptr(), targets.data_ptr(), lse.data_ptr(), dnll.data_ptr(),
-                        dh.data_ptr(), dw.data_ptr() if dw is not None else None, N, V, D, _dtype_code(h),
-                        ws.data_ptr(), ws.numel(), _stream())
+    ws, ws_bytes = _workspace(workspace, nbytes, dev, 256)
+    with _on(dev):
+        st = lib.fa_lce_bwd(h.data_ptr(), w.data_ptr(), targets.data_ptr(), lse.data_ptr(), dnll.data_ptr(),
+                            dh.data_ptr(), dw.data_ptr() if dw is not None else None, N, V, D, _dtype_code(h),
+                            ws.data_ptr(), ws_bytes, _stream())
     if st:
         raise FaError(st, "fa_lce_bwd")
     return dh, dw

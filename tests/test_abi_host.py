@@ -213,3 +213,19 @@ def test_lce_workspace_sizes(lib):
     assert ws(8192, 151936, 4096, 1) == 8192 * 8192 * 2 + 8192 * 4096 * 4
     assert ws(100, 5000, 256, 1) == 100 * 8192 * 2
     assert ws(100, 5000, 255, 1) == 0 and ws(0, 5000, 256, 0) == 0
+
+
+def test_python_binding_refuses_host_tensors():
+    """The binding checks its tensors before touching the library: host
+    (CPU) tensors are refused with a ValueError, never passed on as device
+    pointers."""
+    torch = pytest.importorskip("torch")
+    import memory_efficient_attention_amd as fa
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="CUDA"):
+        fa.fa_fwd(q, q, q)
+    with pytest.raises(ValueError, match="CUDA"):
+        fa.fa_bwd(q, q, q, q, q, torch.zeros(1, 2, 16))
+    h = torch.zeros(8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="CUDA"):
+        fa.fa_lce_fwd(h, h, torch.zeros(8, dtype=torch.int32))

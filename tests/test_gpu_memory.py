@@ -89,3 +89,25 @@ def test_loss_layer_allocates_nothing_and_workspace_is_far_below_logits():
     say(f"  loss workspace fwd {wf} B, bwd {wb} B; bf16 logits {logits} B; extra device bytes {extra}")
     assert extra == 0
     assert wf < logits // 50 and wb < logits // 8
+
+
+def test_caller_workspace_is_checked_not_replaced():
+    """A caller that passes a workspace gets no allocation: one too small, or
+    in host memory, is refused instead of silently replaced."""
+    import torch
+    import memory_efficient_attention_amd as fa
+    B, H, N, D = 1, 2, 300, 64
+    q, k, v, do = (torch.randn(B, H, N, D, device="cuda").bfloat16() for _ in range(4))
+    seg = (torch.arange(N, device="cuda", dtype=torch.int32) // 50).reshape(1, N).contiguous()
+    need = fa.fa_workspace_bytes(B, H, N, D, True, True)
+    o, lse = fa.fa_fwd(q, k, v, seg)
+    small = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="bytes"):
+        fa.fa_bwd(q, k, v, o, do, lse, seg, workspace=small)
+    with pytest.raises(ValueError, match="workspace is on"):
+        fa.fa_bwd(q, k, v, o, do, lse, seg, workspace=torch.empty(need, dtype=torch.uint8))
+    exact = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, seg, workspace=exact)
+    dq2, dk2, dv2 = fa.fa_bwd(q, k, v, o, do, lse, seg)
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert bool((a == b).all())
