@@ -35,7 +35,9 @@
  *     workspace 256-byte aligned.
  *   - The caller owns every buffer, including the workspace (size from
  *     fa_workspace_bytes).  The library never allocates device memory and keeps
- *     no state between calls beyond a per-device architecture check.
+ *     no state between calls beyond a per-device record of the architecture
+ *     check and the compute-unit count (which sets the launch order of small
+ *     causal grids, never a result).
  *   - Calls are asynchronous on `stream` (a hipStream_t of the current device;
  *     NULL means the default stream).  Outputs are overwritten, never
  *     accumulated; inputs are only read.  Two calls that share a workspace
