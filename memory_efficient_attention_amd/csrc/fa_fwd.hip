@@ -25,15 +25,16 @@
 namespace fa {
 
 //
-// KSUB = 2 (8-wave bf16 workgroups): each ring slot holds two key tiles,
-// walked one after the other with the same registers, so a wave does twice
-// the MFMAs per barrier; every operation on every row happens in the same
-// order as with one tile per slot.
-template <typename T, int D, bool CAUSAL, int NW>
+// KSUB = 2 (8-wave bf16 workgroups of dense calls): each ring slot holds two
+// key tiles, so a wave does twice the MFMAs per barrier, and the second
+// tile's scores are issued together with the first tile's softmax (see the
+// slot body).  Every operation on every row happens in the same order as
+// with one tile per slot.
+template <typename T, int D, bool CAUSAL, int NW, int KSUB = 1>
 __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const FwdParams p) {
   constexpr int BM = NW * 32, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
-  constexpr int KSUB = (NW == 8 && sizeof(T) == 2) ? FA_KSUB : 1;
+  static_assert(KSUB == 1 || (KSUB == 2 && NW == 8 && sizeof(T) == 2), "two-tile slots: 8-wave bf16");
   constexpr int SR = KSUB * BN;   // key rows per ring slot
   // K is read only along rows (row-only layout), V only transposed (DUAL).
   using LK = Layout<T, D, false>;
@@ -56,7 +57,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
   // Which (batch, head, query tile), and the key tiles to walk.  Packed: the
   // longest-first work list.  Dense: each XCD takes a contiguous range of
   // heads, the last (for causal, longest) query tiles first.
-  const bool packed = p.seg != nullptr;
+  // two-tile instances are launched for dense calls only (no packed code)
+  const bool packed = KSUB == 1 && p.seg != nullptr;
   // (mirrored blocks: see mirror_block)
   int bh, b, kt_lo = 0, kt_hi, qw0;
   if (packed) {
@@ -139,6 +141,156 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
   settle(segq_first);
   settle(segq_last);
 
+  // ---- two-tile slot body (dense calls).  Probabilities overwrite their
+  // scores in place, so a tile's probabilities cost no second register block;
+  // a tile that takes the rare path has its scores recomputed from LDS first
+  // (same MFMAs in the same order, so the same values).  The registers saved
+  // let a wave issue the first tile's P V MFMAs in one block with the second
+  // tile's exponentials, so its matrix and vector work overlap.  (Issuing
+  // the second tile's scores with the first tile's softmax as well needs two
+  // score blocks at once: it spills at head_dim 128 and measured 3-5 %
+  // slower at 96 and 64.)
+  auto scores = [&](f32x16 (&s)[KB], const FA_LDS char* Ks_, int rs) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) mma(s[kb], frag_row<T, D, false>(Ks_, rbase, rs + 32 * kb, ks), qf[ks]);
+    }
+  };
+  auto mask_dense = [&](f32x16 (&s)[KB], int k0) {
+    const int L = (CAUSAL ? min(qi, N - 1) : N - 1) - (k0 + 4 * h);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (!(32 * kb + 8 * (r >> 2) + (r & 3) <= L)) s[kb][r] = -INFINITY;
+  };
+  // probabilities against the current reference, in place; returns the
+  // lane's partial row sum
+  auto optimistic = [&](f32x16 (&s)[KB], float (&ls)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls[r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = exp2_fast(fmaf(s[kb][r], c, -msc));
+        s[kb][r] = e;
+        ls[r & 3] += e;
+      }
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  // the rare path on the tile's scores: move the references, rescale O and
+  // the sums, probabilities in place
+  auto rare = [&](f32x16 (&s)[KB], float (&ls)[4]) {
+    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], s[kb][r]);
+    float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+    tmax = fmaxf(tmax, other_half(tmax));
+    const float tsc = tmax * c;
+    const bool grow = tsc > msc;
+    const float alpha = grow ? exp2_fast(msc - tsc) : 1.f;
+    msc = grow ? tsc : msc;
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    const float mref = (msc == -INFINITY) ? 0.f : msc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls[r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = exp2_fast(fmaf(s[kb][r], c, -mref));
+        s[kb][r] = e;
+        ls[r & 3] += e;
+      }
+  };
+  auto to_frags = [&](const f32x16 (&s)[KB], frag_t<T> (&pf)[KB][2]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      pf[kb][0] = acc_frag<T>(s[kb], 0);
+      pf[kb][1] = acc_frag<T>(s[kb], 1);
+    }
+  };
+  auto pv = [&](const frag_t<T> (&pf)[KB][2], const FA_LDS char* Vs_, int rs) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+          mma(oacc[db], frag_col<T, D>(Vs_, cbase, rs + 32 * kb + 16 * kc, 32 * db), pf[kb][kc]);
+  };
+  // Interleave of one overlapped block: NM MFMAs, each with its RD LDS
+  // fragment reads issued a step ahead, and the vector work spread between
+  // them, so few fragments are in flight at once.
+  auto interleave = [&](auto nm, auto rd) {
+    constexpr int NM = decltype(nm)::value, RD = decltype(rd)::value;
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + 1 < NM) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+  };
+  // slot of key tiles kt0 and kt0 + 1 (the second may lie past kt_hi)
+  auto slot2 = [&](const FA_LDS char* Ks_, const FA_LDS char* Vs_, int kt0) {
+    const int ka = kt0 * BN, kb1 = ka + BN;
+    if (qw0 >= N || (CAUSAL && ka > qlast)) return;   // the second tile is invisible too
+    const bool has1 = kt0 + 1 <= kt_hi && !(CAUSAL && kb1 > qlast);
+    const bool full0 = (ka + BN <= N) && (!CAUSAL || ka + BN - 1 <= qw0);
+    const bool full1 = (kb1 + BN <= N) && (!CAUSAL || kb1 + BN - 1 <= qw0);
+    f32x16 s0[KB], s1[KB];
+    float ls0[4], ls1[4];
+    scores(s0, Ks_, 0);
+    if (!full0) mask_dense(s0, ka);
+    // first tile's softmax (a row with no reference yet takes the rare path
+    // directly)
+    const bool fresh = __builtin_amdgcn_ballot_w64(msc == -INFINITY) != 0;
+    if (fresh) {
+      rare(s0, ls0);
+    } else {
+      const float lpart = optimistic(s0, ls0);
+      if (__builtin_amdgcn_ballot_w64(!(lpart < GROW_LIMIT)) != 0) {
+        scores(s0, Ks_, 0);
+        if (!full0) mask_dense(s0, ka);
+        rare(s0, ls0);
+      }
+    }
+    lsum += (ls0[0] + ls0[1]) + (ls0[2] + ls0[3]);
+    frag_t<T> pf0[KB][2];
+    to_frags(s0, pf0);
+    if (!has1) {
+      pv(pf0, Vs_, 0);
+      return;
+    }
+    // first tile's P V with the second tile's softmax alongside; a row
+    // without a reference cannot remain here (the first tile gave every row
+    // one), and any overflow sends the tile down the rare path
+    scores(s1, Ks_, BN);
+    if (!full1) mask_dense(s1, kb1);
+    pv(pf0, Vs_, 0);
+    const float lpart1 = optimistic(s1, ls1);
+    interleave(int_c<DB * KB * 2>{}, int_c<2>{});
+    if (__builtin_amdgcn_ballot_w64(!(lpart1 < GROW_LIMIT)) != 0) {
+      scores(s1, Ks_, BN);
+      if (!full1) mask_dense(s1, kb1);
+      rare(s1, ls1);
+    }
+    lsum += (ls1[0] + ls1[1]) + (ls1[2] + ls1[3]);
+    frag_t<T> pf1[KB][2];
+    to_frags(s1, pf1);
+    pv(pf1, Vs_, BN);
+  };
+
   for (int js = 0; js < nst; ++js) {
     const int buf = js % S;
     wait_tiles<LPT, S - 2>(nst - 1 - js);
@@ -148,6 +300,10 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
     const FA_LDS char* Ks = smem + buf * TK;
     const FA_LDS char* Vs = smem + S * TK + buf * TV;
     const FA_LDS int* segs = (const FA_LDS int*)(smem + S * (TK + TV) + buf * SR * 4);
+    if constexpr (KSUB == 2) {
+      slot2(Ks, Vs, kt_lo + 2 * js);
+      continue;
+    }
 #pragma unroll
     for (int sub = 0; sub < KSUB; ++sub) {
     const int kt = kt_lo + KSUB * js + sub;
@@ -290,7 +446,12 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, int nw,
     constexpr int DD = decltype(d)::value, NW = decltype(w)::value;
     constexpr bool C = decltype(c)::value;
     const long long total = (long long)p.B * p.H * p.nqt;
-    hipLaunchKernelGGL((fwd_kernel<T, DD, C, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    // 8-wave bf16 workgroups of dense calls take two key tiles per slot
+    constexpr int KS2 = (NW == 8 && sizeof(T) == 2) ? FA_KSUB : 1;
+    if (KS2 > 1 && p.seg == nullptr)
+      hipLaunchKernelGGL((fwd_kernel<T, DD, C, NW, KS2>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, DD, C, NW, 1>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
   });
 }
