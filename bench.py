@@ -465,8 +465,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this attention path runs on one GPU (one process, one device); runs on more "
-              "than one GPU are not part of it.  How it would shard across GPUs (by batch and head, "
-              "no exchange) is described in DESIGN.md.", file=sys.stderr)
+              "than one GPU are not part of it.  It would shard across GPUs by batch and head, with "
+              "no exchange between them.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
