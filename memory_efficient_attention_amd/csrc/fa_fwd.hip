@@ -26,9 +26,9 @@ namespace fa {
 
 //
 // KSUB = 2 (8-wave bf16 workgroups of dense calls): each ring slot holds two
-// key tiles, so a wave does twice the MFMAs per barrier, and the second
-// tile's scores are issued together with the first tile's softmax (see the
-// slot body).  Every operation on every row happens in the same order as
+// key tiles, so a wave does twice the MFMAs per barrier, and the first
+// tile's P V MFMAs are issued together with the second tile's softmax (see
+// the slot body).  Every operation on every row happens in the same order as
 // with one tile per slot.
 template <typename T, int D, bool CAUSAL, int NW, int KSUB = 1>
 __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const FwdParams p) {
