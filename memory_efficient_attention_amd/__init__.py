@@ -29,6 +29,7 @@ __all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_workspace_bytes", "fa_check_seg",
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_BF16, FA_FP32 = 0, 1
+FA_ERR_SEG = 8
 _lib = None
 
 
@@ -173,10 +174,24 @@ def _kv_heads(q, k) -> int:
     return int(k.shape[1])
 
 
-def fa_fwd(q, k, v, seg=None, scale=None, causal=True, out=None, lse=None, workspace=None):
+def _segment_flag(ws, seg, check_seg, where):
+    """With check_seg, read the device's segment-order flag (workspace word 0,
+    set by the schedule when ids decrease along a row) and raise FaError
+    (FA_ERR_SEG) if it is set.  This waits for the call to finish."""
+    if not check_seg or seg is None:
+        return
+    import torch
+    if int(ws[:4].view(torch.int32).item()) != 0:
+        raise FaError(FA_ERR_SEG, where)
+
+
+def fa_fwd(q, k, v, seg=None, scale=None, causal=True, out=None, lse=None, workspace=None,
+           check_seg=False):
     """Forward pass; returns (o, lse).  q is (B, H, N, D); k and v are
     (B, Hkv, N, D) with Hkv dividing H (query head h reads key/value head
-    h // (H // Hkv))."""
+    h // (H // Hkv)).  check_seg: after the call, wait for it and raise
+    FaError if the device found segment ids that decrease along a row (their
+    outputs are then unspecified)."""
     import torch
     B, H, N, D = q.shape
     Hkv = _kv_heads(q, k)
@@ -199,12 +214,13 @@ def fa_fwd(q, k, v, seg=None, scale=None, causal=True, out=None, lse=None, works
                         _dtype_code(q), ws.data_ptr() if ws is not None else None, ws_bytes, _stream())
     if st:
         raise FaError(st, "fa_fwd")
+    _segment_flag(ws, seg, check_seg, "fa_fwd")
     return o, lse_t
 
 
 def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=None, dv=None,
-           workspace=None, events=None):
-    """Backward pass from dO; returns (dq, dk, dv).
+           workspace=None, events=None, check_seg=False):
+    """Backward pass from dO; returns (dq, dk, dv).  check_seg as in fa_fwd.
 
     ``events``: optional sequence of 4 raw hipEvent_t handles (ints or None)
     recorded between the backward kernels (fa_bwd_timed in the C ABI)."""
@@ -240,6 +256,7 @@ def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=N
             st = lib.fa_bwd_timed(*args, ev)
     if st:
         raise FaError(st, "fa_bwd")
+    _segment_flag(ws, seg, check_seg, "fa_bwd")
     return dq, dk, dv
 
 

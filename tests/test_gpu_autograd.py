@@ -44,7 +44,8 @@ def test_flash_attention_autograd(packed):
         assert bool((a == b).all()), f"{name}: autograd differs from fa_bwd"
     o_r, lse_r = attention_forward(t["q"], t["k"], t["v"], seg_np, scale, True)
     g_r = attention_backward(t["q"], t["k"], t["v"], t["do"], seg_np, scale, True, o=o_r, lse=lse_r)
-    check_o(down(out), o_r, "bf16")
+    pv_r, _ = attention_forward(t["q"], t["k"], np.abs(t["v"]), seg_np, scale, True)
+    check_o(down(out), o_r, "bf16", pv_abs=pv_r)
     for name, g, r in zip(("dq", "dk", "dv"), (q.grad, k.grad, v.grad), g_r):
         check_grad(down(g), r, "bf16", name)
 

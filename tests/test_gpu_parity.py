@@ -19,8 +19,8 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_helpers import (check_grad, check_lse, check_o, down, run_gpu, say, upload,
-                         upload_seg)
+from gpu_helpers import (check_grad, check_lse, check_o, down, run_gpu, say, sees_only_itself, upload,
+                         upload_seg, zero_grad_bounds)
 from oracle import attention_backward, attention_forward, attention_rows
 
 pytestmark = pytest.mark.gpu
@@ -39,16 +39,23 @@ def gpu():
 
 def _oracle_full(t, seg, scale, causal):
     o, lse = attention_forward(t["q"], t["k"], t["v"], seg, scale, causal)
+    pv, _ = attention_forward(t["q"], t["k"], np.abs(t["v"]), seg, scale, causal)   # P|V|, for o_bound
     dq, dk, dv = attention_backward(t["q"], t["k"], t["v"], t["do"], seg, scale, causal, o=o, lse=lse)
-    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, pv=pv)
 
 
 def _compare(out, ref, dtype, sl=(slice(None),), tag=""):
     """Compare GPU outputs (device tensors) against oracle arrays on index `sl`."""
     o = down(out["o"][sl])
-    check_o(o, ref["o"], dtype, f"O{tag}")
+    check_o(o, ref["o"], dtype, f"O{tag}", ref["pv"])
     check_lse(down(out["lse"][sl]), ref["lse"], dtype)
-    errs = [check_grad(down(out[n][sl]), ref[n], dtype, f"{n}{tag}") for n in ("dq", "dk", "dv")]
+    # dQ and dK are exactly zero where every row sees only itself: checked
+    # against the absolute bound of the fp32 cancellation instead
+    zero = sees_only_itself(out)
+
+    def zb(n):
+        return (lambda: zero_grad_bounds(out, out["scale"])[n][sl]) if zero and n != "dv" else None
+    errs = [check_grad(down(out[n][sl]), ref[n], dtype, f"{n}{tag}", zero_bound=zb(n)) for n in ("dq", "dk", "dv")]
     return errs
 
 
@@ -165,7 +172,7 @@ def test_rising_and_falling_scores(D, dtype):
     for sg in (None, seg):
         out = run_gpu(t, sg, dtype, scale, True)
         ref = _oracle_full(t, sg, scale, True)
-        check_o(down(out["o"]), ref["o"], dtype)
+        check_o(down(out["o"]), ref["o"], dtype, pv_abs=ref["pv"])
         check_lse(down(out["lse"]), ref["lse"], dtype)
         for n in grads:
             check_grad(down(out[n]), ref[n], dtype, n)
@@ -300,7 +307,8 @@ def test_causal_16k():
     o_all, lse_all = down(out["o"]), down(out["lse"])
     for hh in range(w.H):
         o_r, l_r = attention_rows(t["q"][0, hh], t["k"][0, hh], t["v"][0, hh], rows, None, w.scale, True)
-        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}")
+        pv_r, _ = attention_rows(t["q"][0, hh], t["k"][0, hh], np.abs(t["v"][0, hh]), rows, None, w.scale, True)
+        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}", pv_r)
         check_lse(lse_all[0, hh, rows], l_r, w.dtype)
     _invariants(out)
 
@@ -315,7 +323,8 @@ def test_single_segment_8k_bitwise_equals_causal():
         assert bool((packed[n] == causal[n]).all()), f"{n}: single-segment packed != causal"
     rows = np.array([0, 5, 100, 4097, 8191])
     o_r, l_r = attention_rows(t["q"][0, 3], t["k"][0, 3], t["v"][0, 3], rows, None, w.scale, True)
-    check_o(down(packed["o"][0, 3, rows]), o_r, w.dtype)
+    pv_r, _ = attention_rows(t["q"][0, 3], t["k"][0, 3], np.abs(t["v"][0, 3]), rows, None, w.scale, True)
+    check_o(down(packed["o"][0, 3, rows]), o_r, w.dtype, pv_abs=pv_r)
     check_lse(down(packed["lse"][0, 3, rows]), l_r, w.dtype)
 
 
@@ -349,7 +358,9 @@ def test_packed_long_documents_64k():
         rows = np.unique(np.concatenate([starts, starts + 1, rng.integers(0, w.N, 12), [w.N - 1]]))
         rows = rows[rows < w.N]
         o_r, l_r = attention_rows(t["q"][0, hh], t["k"][0, hh], t["v"][0, hh], rows, seg[0], w.scale, True)
-        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}")
+        pv_r, _ = attention_rows(t["q"][0, hh], t["k"][0, hh], np.abs(t["v"][0, hh]), rows, seg[0], w.scale,
+                                 True)
+        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}", pv_r)
         check_lse(lse_all[0, hh, rows], l_r, w.dtype)
     # whole segments: a packed row equals each segment run alone
     order = np.argsort(lens)
@@ -396,7 +407,7 @@ def test_grouped_query_heads_8k():
     tb = {n: (t[n][:, g:g + 1] if n in ("k", "v") else t[n][:, g * G:(g + 1) * G]) for n in t}
     ref = _oracle_full(tb, None, w.scale, True)
     o, lse = down(out["o"][:, g * G:(g + 1) * G]), down(out["lse"][:, g * G:(g + 1) * G])
-    check_o(o, ref["o"], w.dtype)
+    check_o(o, ref["o"], w.dtype, pv_abs=ref["pv"])
     check_lse(lse, ref["lse"], w.dtype)
     check_grad(down(out["dq"][:, g * G:(g + 1) * G]), ref["dq"], w.dtype, "dq")
     check_grad(down(out["dk"][:, g:g + 1]), ref["dk"], w.dtype, "dk")
@@ -407,7 +418,9 @@ def test_grouped_query_heads_8k():
     for hh in range(w.H):
         o_r, l_r = attention_rows(t["q"][0, hh], t["k"][0, hh // G], t["v"][0, hh // G], rows, None,
                                   w.scale, True)
-        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}")
+        pv_r, _ = attention_rows(t["q"][0, hh], t["k"][0, hh // G], np.abs(t["v"][0, hh // G]), rows, None,
+                                 w.scale, True)
+        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}", pv_r)
         check_lse(lse_all[0, hh, rows], l_r, w.dtype)
     _invariants(out)
     # the dK/dV teams add their halves of each group in a fixed order
@@ -433,7 +446,7 @@ def test_maximum_sequence_length():
         say(f"  document {d}: rows {r0}..{r1 - 1}")
         tb = {n: t[n][:, :, r0:r1] for n in t}
         ref = _oracle_full(tb, None, 0.125, True)
-        check_o(down(out["o"][:, :, r0:r1]), ref["o"], "bf16")
+        check_o(down(out["o"][:, :, r0:r1]), ref["o"], "bf16", pv_abs=ref["pv"])
         check_lse(down(out["lse"][:, :, r0:r1]), ref["lse"], "bf16")
         for n in ("dq", "dk", "dv"):
             check_grad(down(out[n][:, :, r0:r1]), ref[n], "bf16", f"{n} document {d}")
@@ -456,6 +469,59 @@ def test_head_dim_96_8k():
     o_all, lse_all = down(out["o"]), down(out["lse"])
     for hh in range(w.H):
         o_r, l_r = attention_rows(t["q"][0, hh], t["k"][0, hh], t["v"][0, hh], rows, None, w.scale, True)
-        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}")
+        pv_r, _ = attention_rows(t["q"][0, hh], t["k"][0, hh], np.abs(t["v"][0, hh]), rows, None, w.scale, True)
+        check_o(o_all[0, hh, rows], o_r, w.dtype, f"O rows h{hh}", pv_r)
         check_lse(lse_all[0, hh, rows], l_r, w.dtype)
     _invariants(out)
+
+
+def test_decreasing_segment_ids_are_flagged():
+    """Segment ids must be non-decreasing along a row.  A row that breaks this
+    gets unspecified values, but every access stays in bounds (shown for the
+    schedule's index arithmetic by tests/test_schedule_model.py), the other
+    rows are untouched, and the device sets workspace word 0, which the
+    binding's check_seg turns into FaError (FA_ERR_SEG).  Valid ids leave the
+    word at 0."""
+    import torch
+    import memory_efficient_attention_amd as fa
+    B, H, N, D = 2, 2, 300, 64
+    scale = 0.125
+    say(f"decreasing segment ids B{B} H{H} N{N} D{D} bf16: row 1 bad, row 0 valid")
+    t = workloads.make_tensors(B, H, N, D, "bf16", 93)
+    good = workloads.random_segments(B, N, 93, max_len=70)
+    bad = good.copy()
+    bad[1] = bad[1][::-1].copy()                       # row 1: ids decrease
+    assert fa.fa_check_seg(good) is None
+    with pytest.raises(fa.FaError):
+        fa.fa_check_seg(bad)
+    q, k, v, do = (upload(t[n], "bf16") for n in ("q", "k", "v", "do"))
+    dev = q.device
+    ws_f = torch.zeros(fa.fa_workspace_bytes(B, H, N, D, True, False), dtype=torch.uint8, device=dev)
+    ws_b = torch.zeros(fa.fa_workspace_bytes(B, H, N, D, True, True), dtype=torch.uint8, device=dev)
+
+    def flag(ws):
+        torch.cuda.synchronize()
+        return int(ws[:4].view(torch.int32).item())
+
+    for seg, want in ((bad, 1), (good, 0)):
+        sg = upload_seg(seg)
+        o, lse = fa.fa_fwd(q, k, v, sg, scale, True, workspace=ws_f)
+        assert flag(ws_f) == want, f"forward flag {flag(ws_f)}, expected {want}"
+        dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, sg, scale, True, workspace=ws_b)
+        assert flag(ws_b) == want, f"backward flag {flag(ws_b)}, expected {want}"
+        # row 0 is valid either way and must match the oracle
+        t0 = {n: x[0:1] for n, x in t.items()}
+        ref = _oracle_full(t0, seg[0:1], scale, True)
+        out = dict(q=q[0:1], k=k[0:1], v=v[0:1], do=do[0:1], o=o[0:1], lse=lse[0:1], dq=dq[0:1],
+                   dk=dk[0:1], dv=dv[0:1], seg=sg[0:1], scale=scale)
+        _compare(out, ref, "bf16", tag=f"[row 0, row 1 {'bad' if want else 'valid'}]")
+        if want:
+            with pytest.raises(fa.FaError) as e:
+                fa.fa_fwd(q, k, v, sg, scale, True, workspace=ws_f, check_seg=True)
+            assert e.value.status == fa.FA_ERR_SEG
+            with pytest.raises(fa.FaError) as e:
+                fa.fa_bwd(q, k, v, o, do, lse, sg, scale, True, workspace=ws_b, check_seg=True)
+            assert e.value.status == fa.FA_ERR_SEG
+        else:
+            fa.fa_fwd(q, k, v, sg, scale, True, workspace=ws_f, check_seg=True)
+            fa.fa_bwd(q, k, v, o, do, lse, sg, scale, True, workspace=ws_b, check_seg=True)
