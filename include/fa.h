@@ -69,7 +69,9 @@ typedef enum fa_status {
     FA_ERR_SCALE = 7,      /* scale is not a finite positive number */
     FA_ERR_SEG = 8,        /* fa_check_seg: ids decrease somewhere along a row */
     FA_ERR_HIP = 9,        /* a HIP call or kernel launch failed */
-    FA_ERR_DEVICE = 10     /* the current device is not a gfx950 GPU (or none) */
+    FA_ERR_DEVICE = 10,    /* the current device is not a gfx950 GPU (or none) */
+    FA_ERR_SCRATCH = 11    /* fa_bwd_noalloc: the shape needs more workspace than
+                              FA_NOALLOC_MAX_BYTES */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -146,6 +148,29 @@ fa_status fa_bwd_timed(const void* q, const void* k, const void* v, const void* 
                        float scale, int causal, void* dq, void* dk, void* dv,
                        int B, int H, int Hkv, int N, int D, fa_dtype dtype,
                        void* ws, size_t ws_bytes, void* stream, void* const* events);
+
+/*
+ * fa_bwd without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * training loops, harnesses that forbid hipMalloc.  The workspace is a
+ * static device array of FA_NOALLOC_MAX_BYTES inside the library, one per GPU,
+ * held from the first call on that GPU until the process ends; the call makes
+ * no hipMalloc, hipFree or other allocating call.  Arguments, outputs and
+ * results are those of fa_bwd (the same kernels run), plus FA_ERR_SCRATCH,
+ * returned before any HIP call, when fa_workspace_bytes(B, H, N, D,
+ * seg != NULL, 1) exceeds FA_NOALLOC_MAX_BYTES (for example B * H * N above
+ * about 4 million rows without seg).  Nothing in the array needs to start at
+ * zero: every call writes each word it later reads.  All calls on one GPU
+ * share its array, which keeps the last call's contents: calls that overlap
+ * on one GPU (two streams, or two threads) race and must be ordered by the
+ * caller.  FA_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define FA_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, const int32_t* seg,
+                         float scale, int causal, void* dq, void* dk, void* dv,
+                         int B, int H, int Hkv, int N, int D, fa_dtype dtype,
+                         void* stream);
 
 /*
  * Host-side precondition check of a HOST copy of seg: FA_OK when every row is

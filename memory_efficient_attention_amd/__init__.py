@@ -22,7 +22,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_workspace_bytes", "fa_check_seg",
+__all__ = ["FaError", "fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_workspace_bytes", "fa_check_seg",
            "fa_status_string", "flash_attention", "fa_lce_fwd", "fa_lce_bwd", "fa_lce_workspace_bytes",
            "linear_cross_entropy", "library_path", "load_library", "FA_BF16", "FA_FP32"]
 
@@ -30,6 +30,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_BF16, FA_FP32 = 0, 1
 FA_ERR_SEG = 8
+FA_ERR_SCRATCH = 11
+FA_NOALLOC_MAX_BYTES = 32 << 20
 _lib = None
 
 
@@ -69,6 +71,8 @@ def load_library():
     lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp,
                                  vp]
     lib.fa_bwd_timed.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_lce_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_lce_workspace_bytes.restype = sz
     lib.fa_lce_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]
@@ -257,6 +261,39 @@ def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=N
     if st:
         raise FaError(st, "fa_bwd")
     _segment_flag(ws, seg, check_seg, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=None, dv=None):
+    """fa_bwd without a workspace: the library uses its own static device
+    array (FA_NOALLOC_MAX_BYTES per GPU), so the call allocates nothing when
+    dq, dk and dv are given.  Calls that overlap on one GPU race on that
+    array.  Shapes needing more workspace raise FaError (FA_ERR_SCRATCH)."""
+    import torch
+    B, H, N, D = q.shape
+    Hkv = _kv_heads(q, k)
+    dev = q.device
+    for name, t in (("q", q), ("o", o), ("do", do)):
+        _check_tensor(name, t, (B, H, N, D), q.dtype, dev)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, Hkv, N, D), q.dtype, dev)
+    _check_tensor("lse", lse, (B, H, N), torch.float32, dev)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensor("dq", dq, (B, H, N, D), q.dtype, dev)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, (B, Hkv, N, D), q.dtype, dev)
+    seg_p = _seg_ptr(seg, B, N, dev)
+    lib = load_library()
+    with _on(dev):
+        st = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                lse.data_ptr(), seg_p, ctypes.c_float(scale), int(bool(causal)),
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, D,
+                                _dtype_code(q), _stream())
+    if st:
+        raise FaError(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

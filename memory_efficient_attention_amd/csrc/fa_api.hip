@@ -66,6 +66,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 std::mutex g_mu;
 signed char g_dev_ok[64];
 int g_dev_cus[64];   // compute units of each checked device
+void* g_scratch_ptr[64];   // device address of `scratch` on each device, once looked up
 
 fa_status device_ok() {
   int dev = -1;
@@ -184,7 +185,33 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, const int32
   return FA_OK;
 }
 
+// Backward workspace of fa_bwd_noalloc: a fixed array in device memory,
+// one copy per GPU, alive until the process ends.  Host code never uses its
+// name as an address (on the host the name is only a stand-in); the device
+// address comes from hipGetSymbolAddress, per device.
+static __device__ __attribute__((aligned(256))) char scratch[FA_NOALLOC_MAX_BYTES];
+
 namespace {
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there and kept; nullptr if the lookup fails.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 bool record(void* const* events, int i, hipStream_t s) {
   if (!events || !events[i]) return true;
@@ -291,6 +318,20 @@ FA_API fa_status fa_bwd_timed(const void* q, const void* k, const void* v, const
                               void* ws, size_t ws_bytes, void* stream, void* const* events) {
   return bwd_impl(q, k, v, o, dO, lse, seg, scale, causal, dq, dk, dv, B, H, Hkv, N, D, dtype, ws, ws_bytes,
                   stream, events);
+}
+
+FA_API fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                const float* lse, const int32_t* seg, float scale, int causal, void* dq,
+                                void* dk, void* dv, int B, int H, int Hkv, int N, int D, fa_dtype dtype,
+                                void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (fa_status st = common_checks(B, H, Hkv, N, D, dtype, scale)) return st;
+  if (layout(B, H, N, seg != nullptr, true).total > FA_NOALLOC_MAX_BYTES) return FA_ERR_SCRATCH;
+  if (fa_status st = device_ok()) return st;
+  void* ws = device_scratch();
+  if (!ws) return FA_ERR_HIP;
+  return bwd_impl(q, k, v, o, dO, lse, seg, scale, causal, dq, dk, dv, B, H, Hkv, N, D, dtype, ws,
+                  FA_NOALLOC_MAX_BYTES, stream, nullptr);
 }
 
 // ---------------------------------------------------------------- linear cross-entropy
@@ -413,6 +454,7 @@ FA_API const char* fa_status_string(fa_status status) {
     case FA_ERR_SEG: return "segment ids decrease along a row";
     case FA_ERR_HIP: return "HIP launch failed";
     case FA_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    case FA_ERR_SCRATCH: return "shape needs more workspace than fa_bwd_noalloc's static scratch (FA_NOALLOC_MAX_BYTES)";
   }
   return "unknown status";
 }

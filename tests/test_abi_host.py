@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE = 0, 1, 2, 3, 4
 FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_SCALE, FA_ERR_SEG, FA_ERR_HIP, FA_ERR_DEVICE = 5, 6, 7, 8, 9, 10
+FA_ERR_SCRATCH = 11
 
 
 @pytest.fixture(scope="module")
@@ -38,12 +39,13 @@ def test_header_status_values_match():
     vals = dict((n, int(v)) for n, v in re.findall(r"\b(FA_\w+)\s*=\s*(\d+)", text))
     assert vals["FA_OK"] == FA_OK and vals["FA_ERR_DEVICE"] == FA_ERR_DEVICE
     assert vals["FA_ERR_ALIGN"] == FA_ERR_ALIGN and vals["FA_ERR_SEG"] == FA_ERR_SEG
+    assert vals["FA_ERR_SCRATCH"] == FA_ERR_SCRATCH
 
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
-    assert declared == ["fa_bwd", "fa_bwd_timed", "fa_check_seg", "fa_fwd", "fa_lce_bwd", "fa_lce_fwd",
-                        "fa_lce_workspace_bytes", "fa_status_string", "fa_workspace_bytes"]
+    assert declared == ["fa_bwd", "fa_bwd_noalloc", "fa_bwd_timed", "fa_check_seg", "fa_fwd", "fa_lce_bwd",
+                        "fa_lce_fwd", "fa_lce_workspace_bytes", "fa_status_string", "fa_workspace_bytes"]
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = sorted(set(re.findall(r" T (fa_\w+)", out)))
     assert exported == declared          # and nothing else leaks out of the library
@@ -110,6 +112,29 @@ def test_bwd_refusals(lib, kw, status):
     assert _bwd(lib, **kw) == status
 
 
+def _bwd_noalloc(lib, q=P, k=P, v=P, o=P, do=P, lse=P, seg=None, scale=0.125, causal=1, dq=P, dk=P, dv=P,
+                 B=1, H=2, Hkv=None, N=64, D=64, dtype=0):
+    Hkv = H if Hkv is None else Hkv
+    return lib.fa_bwd_noalloc(q, k, v, o, do, lse, seg, ctypes.c_float(scale), causal, dq, dk, dv, B, H,
+                              Hkv, N, D, dtype, None)
+
+
+def test_bwd_noalloc_refusals(lib):
+    """The allocation-free backward refuses, before any HIP call, what fa_bwd
+    refuses, and shapes whose workspace exceeds its static array."""
+    import memory_efficient_attention_amd as fa
+    assert _bwd_noalloc(lib, dq=None) == FA_ERR_NULL
+    assert _bwd_noalloc(lib, D=80) == FA_ERR_HEAD_DIM
+    assert _bwd_noalloc(lib, scale=0.0) == FA_ERR_SCALE
+    # the largest row count that fits, and one more 256-byte block than fits
+    # (256 bytes of flags, then two fp32 arrays of B * H * N, each rounded up to 256 bytes)
+    rows = ((fa.FA_NOALLOC_MAX_BYTES - 256) // 2 // 256 * 256) // 4
+    assert lib.fa_workspace_bytes(1, 1, rows, 64, 0, 1) <= fa.FA_NOALLOC_MAX_BYTES
+    assert lib.fa_workspace_bytes(1, 1, rows + 64, 64, 0, 1) > fa.FA_NOALLOC_MAX_BYTES
+    assert _bwd_noalloc(lib, B=1, H=1, N=rows + 64) == FA_ERR_SCRATCH
+    assert _bwd_noalloc(lib, B=64, H=32, N=4096) == FA_ERR_SCRATCH
+
+
 def test_first_failing_check_wins(lib):
     # a null pointer is reported before a bad shape, a bad shape before a bad dtype
     assert _fwd(lib, q=None, B=0, dtype=9) == FA_ERR_NULL
@@ -157,11 +182,11 @@ def test_python_check_seg_raises():
 
 def test_status_strings(lib):
     seen = set()
-    for s in range(0, 11):
+    for s in range(0, 12):
         txt = lib.fa_status_string(s).decode()
         assert txt and txt != "unknown status"
         seen.add(txt)
-    assert len(seen) == 11
+    assert len(seen) == 12
     assert lib.fa_status_string(1234).decode() == "unknown status"
 
 
