@@ -105,7 +105,17 @@ class HipEvents:
 
 
 def alg_flops(kernel: str, D: int, V: int) -> float:
-    """Algorithmic (visible-pair) flops of one launch of each kernel."""
+    """Credited (algorithmic) flops of one launch of each kernel, per visible
+    pair: the step's 14 D is split as the forward's 4 D (S, P V), dQ's 6 D
+    (the backward's one S recompute, dP, dQ) and dK/dV's 4 D (dV, dK).  The
+    second S and dP that dK/dV recomputes are the split design's own cost and
+    are not credited."""
+    return {"fwd": 4.0, "dkdv": 4.0, "dq": 6.0, "pre": 0.0}[kernel] * D * V
+
+
+def executed_flops(kernel: str, D: int, V: int) -> float:
+    """MFMA flops each kernel executes per visible pair (dK/dV computes S,
+    dP, dV and dK: 8 D), for the matrix-unit utilisation next to the credit."""
     return {"fwd": 4.0, "dkdv": 8.0, "dq": 6.0, "pre": 0.0}[kernel] * D * V
 
 
@@ -198,14 +208,34 @@ def cpu_baseline(w, t_np, seg_np, causal=True):
     rows) and the backward (their dQ and their dK, dV contributions), each with
     the explicit mask over all N keys.  Credited flops are 14 * D times the
     visible pairs of the rows done."""
-    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import attention_backward_rows, attention_rows, visible_mask
+    affinity = len(os.sched_getaffinity(0))
+    threads = oracle_threads()
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        r = _cpu_sample(w, t_np, seg_np, causal, attention_rows, attention_backward_rows, visible_mask)
+    r["cores"] = int(used)
+    r["affinity_cores"] = affinity
+    r["blas_env"] = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+    r["sample"] += f"; cores = BLAS threads in use ({used}, set explicitly) of {affinity} in this process's affinity"
+    return r
+
+
+def oracle_threads() -> int:
+    """BLAS threads for the oracle: OMP_NUM_THREADS when set (main() sets it,
+    and OPENBLAS_NUM_THREADS, to the affinity count when absent), capped at
+    the cores this process may run on."""
+    affinity = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+        return max(1, min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity))))
+    except ValueError:
+        return affinity
+
+
+def _cpu_sample(w, t_np, seg_np, causal, attention_rows, attention_backward_rows, visible_mask):
+    import numpy as np
     b = 0
     seg_row = None if seg_np is None else seg_np[b]
     V, nrows, heads, el = 0, 0, set(), 0.0
@@ -226,11 +256,11 @@ def cpu_baseline(w, t_np, seg_np, causal=True):
                 break
         if el >= CPU_TARGET_SECONDS:
             break
-    return {"value": round(14.0 * w.D * V / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": round(14.0 * w.D * V / el / 1e12, 6), "unit": "TFLOP/s", "cores": 0,
             "kind": "oracle",
             "sample": f"{nrows} query rows of batch 0 over {len(heads)} head(s), last rows first, of "
                       f"N={w.N}, D={w.D}: fp64 forward + backward with the explicit mask over all keys "
-                      f"({V} visible pairs, {el:.1f} s); cores = BLAS threads",
+                      f"({V} visible pairs, {el:.1f} s)",
             "seconds": round(el, 2)}
 
 
@@ -251,12 +281,35 @@ def roofline(w, res):
                 traffic = rec["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             traffic = None
+    executed = executed_flops(dom, w.D, res["V"]) / (avg_ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": KERNEL_NAMES[dom],
-            "avg_ms": round(avg_ms, 4), "alg_flops_per_launch": alg}
+            "avg_ms": round(avg_ms, 4), "alg_flops_per_launch": alg,
+            "executed_flops_per_launch": executed_flops(dom, w.D, res["V"]),
+            "executed_tflops": round(executed, 2), "executed_frac": round(executed / peak, 4),
+            "per_kernel_frac": {k: round(alg_flops(k, w.D, res["V"]) / (stage[k] * 1e-3) / 1e12 / peak, 4)
+                                for k in ("fwd", "dkdv", "dq")}}
 
 
 # ---------------------------------------------------------------- modes
+
+def eight_k(steps, warmup):
+    """The 8k half of the metric: causal N=8192 D=128 (B1 H32 bf16) and the
+    same inputs through the packed path as one segment (identical work), with
+    the packed path's overhead over causal."""
+    import workloads
+    w = workloads.get("single_segment_8k")
+    c = run_workload(w, steps, warmup, seg_override=None)
+    p = run_workload(w, steps, warmup)
+    assert c["V"] == p["V"]
+    row = lambda r: {"ms_per_step": round(r["ms"], 4), "step_ms_median": round(r["ms_median"], 4),
+                     "tflops": round(r["tflops"], 2),
+                     "pct_bf16_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+                     "stages_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()}}
+    return {"workload": "B1 H32 N8192 D128 bf16, causal; and the same inputs as one segment through the "
+                        "packed path", "visible_pairs": c["V"], "causal": row(c), "packed_one_segment": row(p),
+            "packed_overhead_vs_causal": round(p["ms"] / c["ms"] - 1.0, 4)}
+
 
 def headline(args):
     import workloads
@@ -284,6 +337,7 @@ def headline(args):
         "pct_bf16_peak": round(100.0 * res["tflops"] / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in res["stage_ms"].items()},
         "roofline": roofline(w, res),
+        "n8k": eight_k(args.steps, args.warmup) if w.name == DEFAULT_WORKLOAD else None,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -445,6 +499,37 @@ def ingest_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload
     print(json.dumps(entry, indent=1))
 
 
+def summarize_trace(path, warmup):
+    """Per-kernel launch statistics from a rocprofv3 --kernel-trace run of
+    this script: the first `warmup` dispatches of each kernel (the untimed
+    warm-up steps) are dropped, the rest summarised (ms)."""
+    import csv
+    import glob
+    import statistics
+    files = glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {path}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name", "")
+                short = next((k for k, n in KERNEL_NAMES.items() if n in name), None)
+                if short is None:
+                    continue
+                per.setdefault(name, []).append((int(r["Start_Timestamp"]),
+                                                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6))
+    out = {}
+    for name, v in per.items():
+        d = [x for _, x in sorted(v)][warmup:]
+        if not d:
+            continue
+        out[name] = {"calls": len(d), "avg_ms": round(statistics.fmean(d), 4),
+                     "median_ms": round(statistics.median(d), 4), "min_ms": round(min(d), 4),
+                     "max_ms": round(max(d), 4)}
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,10 +543,19 @@ def main():
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
                                                            "CAL_WRITE_DIR"),
                     help="write profiles/traffic.json from rocprofv3 counter runs (CPU only)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="per-kernel statistics of a rocprofv3 kernel trace of this script, warm-up dropped")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.warmup)
+        return
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters, args.workload)
         return
+    # the oracle's BLAS threads, set before numpy (through torch) loads them
+    ncpu = str(len(os.sched_getaffinity(0)))
+    os.environ.setdefault("OMP_NUM_THREADS", ncpu)
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", os.environ["OMP_NUM_THREADS"])
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this attention path runs on one GPU (one process, one device); runs on more "

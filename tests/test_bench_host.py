@@ -45,11 +45,25 @@ def test_visible_pairs_at_the_bench_shape():
 
 def test_algorithmic_flops_per_kernel():
     D, V = 128, 1000
+    # credited: the step's 14 D V split as forward 4, dQ 6 (one S recompute,
+    # dP, dQ), dK/dV 4 (dV, dK)
     assert bench.alg_flops("fwd", D, V) == 4 * D * V
-    assert bench.alg_flops("dkdv", D, V) == 8 * D * V
+    assert bench.alg_flops("dkdv", D, V) == 4 * D * V
     assert bench.alg_flops("dq", D, V) == 6 * D * V
-    # the step credits 14 D V; the split kernels execute 18 D V
-    assert sum(bench.alg_flops(k, D, V) for k in ("fwd", "dkdv", "dq")) == 18 * D * V
+    assert sum(bench.alg_flops(k, D, V) for k in ("fwd", "dkdv", "dq")) == 14 * D * V
+    # executed: dK/dV recomputes S and dP as well, 18 D V in all
+    assert bench.executed_flops("dkdv", D, V) == 8 * D * V
+    assert sum(bench.executed_flops(k, D, V) for k in ("fwd", "dkdv", "dq")) == 18 * D * V
+
+
+def test_oracle_threads_follow_the_environment(monkeypatch):
+    n = len(os.sched_getaffinity(0))
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.oracle_threads() == 1
+    monkeypatch.setenv("OMP_NUM_THREADS", str(n + 100))
+    assert bench.oracle_threads() == n
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.oracle_threads() == n
 
 
 def test_more_than_one_gpu_is_refused():
