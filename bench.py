@@ -40,8 +40,8 @@ PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_16k"
-KERNELS = ("fwd", "pre", "dkdv", "dq")
-KERNEL_NAMES = {"fwd": "fwd_kernel", "pre": "bwd_pre_kernel", "dkdv": "dkdv_kernel", "dq": "dq_kernel"}
+KERNELS = ("fwd", "dq", "dkdv")     # in launch order; dQ also computes the per-row D_i
+KERNEL_NAMES = {"fwd": "fwd_kernel", "dq": "dq_kernel", "dkdv": "dkdv_kernel"}
 
 
 # ---------------------------------------------------------------- helpers
@@ -110,18 +110,13 @@ def alg_flops(kernel: str, D: int, V: int) -> float:
     (the backward's one S recompute, dP, dQ) and dK/dV's 4 D (dV, dK).  The
     second S and dP that dK/dV recomputes are the split design's own cost and
     are not credited."""
-    return {"fwd": 4.0, "dkdv": 4.0, "dq": 6.0, "pre": 0.0}[kernel] * D * V
+    return {"fwd": 4.0, "dkdv": 4.0, "dq": 6.0}[kernel] * D * V
 
 
 def executed_flops(kernel: str, D: int, V: int) -> float:
     """MFMA flops each kernel executes per visible pair (dK/dV computes S,
     dP, dV and dK: 8 D), for the matrix-unit utilisation next to the credit."""
-    return {"fwd": 4.0, "dkdv": 8.0, "dq": 6.0, "pre": 0.0}[kernel] * D * V
-
-
-def pre_bytes(B, H, N, D, elt) -> float:
-    # reads O, dO, LSE; writes D_i and the log2 LSE
-    return 2.0 * B * H * N * D * elt + 3.0 * B * H * N * 4
+    return {"fwd": 4.0, "dkdv": 8.0, "dq": 6.0}[kernel] * D * V
 
 
 # ---------------------------------------------------------------- one workload
@@ -160,12 +155,12 @@ def run_workload(w, steps: int, warmup: int, seg_override="keep", causal=True, q
         if evs:
             ev.record(evs[1], stream)
         fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, seg, w.scale, causal, dq=dq, dk=dk, dv=dv,
-                  workspace=ws_b, events=evs[2:6] if evs else None)
+                  workspace=ws_b, events=evs[2:5] if evs else None)
 
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
     for _ in range(warmup):
         step()
-    stage_ev = [[ev.new() for _ in range(6)] for _ in range(steps)]
+    stage_ev = [[ev.new() for _ in range(5)] for _ in range(steps)]
     t0, t1 = ev.new(), ev.new()
     torch.cuda.synchronize()
     ev.record(t0, stream)
@@ -175,14 +170,13 @@ def run_workload(w, steps: int, warmup: int, seg_override="keep", causal=True, q
         step(stage_ev[i])
     ev.record(t1, stream)
     torch.cuda.synchronize()
-    per_step = sorted(ev.ms(e[0], e[5]) for e in stage_ev)
+    per_step = sorted(ev.ms(e[0], e[4]) for e in stage_ev)
     total_ms = sum(per_step) if cold else ev.ms(t0, t1)
     stage = {k: 0.0 for k in KERNELS}
     for e in stage_ev:
         stage["fwd"] += ev.ms(e[0], e[1])
-        stage["pre"] += ev.ms(e[2], e[3])
+        stage["dq"] += ev.ms(e[2], e[3])
         stage["dkdv"] += ev.ms(e[3], e[4])
-        stage["dq"] += ev.ms(e[4], e[5])
     stage = {k: v / steps for k, v in stage.items()}
     ev.close()
     ms = total_ms / steps
@@ -415,9 +409,9 @@ def report_all(args):
         rows.append(row)
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()}),
               flush=True)
-    print("\n| workload | ms fwd+bwd (mean) | median | min | fwd | pre | dK/dV | dQ | eff. TFLOP/s | % peak | "
+    print("\n| workload | ms fwd+bwd (mean) | median | min | fwd | dQ (with D_i) | dK/dV | eff. TFLOP/s | % peak | "
           "packed speedup vs causal (visible ratio) |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    print("|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
         s = r["stages"]
         sp = (f"{r['speedup_vs_causal']:.2f}x ({r['visible_ratio']:.2f}x) against causal {r['causal_ms']:.3f} ms "
@@ -426,7 +420,7 @@ def report_all(args):
         if "cold_ms" in r:
             sp += f"; cache-cold {r['cold_ms']:.3f} ms"
         print(f"| {r['workload']} | {r['ms']:.3f} | {r['ms_median']:.3f} | {r['ms_min']:.3f} | {s['fwd']:.3f} | "
-              f"{s['pre']:.3f} | {s['dkdv']:.3f} | {s['dq']:.3f} | {r['tflops']:.1f} | "
+              f"{s['dq']:.3f} | {s['dkdv']:.3f} | {r['tflops']:.1f} | "
               f"{100 * r['tflops'] / PEAK_BF16_TFLOPS:.1f} | {sp} |")
 
 

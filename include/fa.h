@@ -136,12 +136,12 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
 /*
  * fa_bwd with per-stage HIP events, for profiling callers that need the time
  * of each backward kernel on its own stream.  `events` is NULL (then this is
- * fa_bwd) or points to 4 hipEvent_t handles, each may be NULL, created by the
+ * fa_bwd) or points to 3 hipEvent_t handles, each may be NULL, created by the
  * caller on the current device.  They are recorded on `stream`: events[0]
- * before the D_i preprocess kernel, events[1] before the dK/dV kernel,
- * events[2] before the dQ kernel, events[3] after it.  Any segment schedule
- * kernels run before events[0].  Same arguments and errors as fa_bwd, plus
- * FA_ERR_HIP if recording an event fails.
+ * before the dQ kernel (which also computes D_i), events[1] after it, before
+ * the dK/dV kernel, events[2] after that.  Any segment schedule kernels run
+ * before events[0].  Same arguments and errors as fa_bwd, plus FA_ERR_HIP if
+ * recording an event fails.
  */
 fa_status fa_bwd_timed(const void* q, const void* k, const void* v, const void* o,
                        const void* dO, const float* lse, const int32_t* seg,

@@ -226,8 +226,9 @@ def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=N
            workspace=None, events=None, check_seg=False):
     """Backward pass from dO; returns (dq, dk, dv).  check_seg as in fa_fwd.
 
-    ``events``: optional sequence of 4 raw hipEvent_t handles (ints or None)
-    recorded between the backward kernels (fa_bwd_timed in the C ABI)."""
+    ``events``: optional sequence of 3 raw hipEvent_t handles (ints or None)
+    recorded before dQ, between dQ and dK/dV, and after dK/dV
+    (fa_bwd_timed in the C ABI)."""
     import torch
     B, H, N, D = q.shape
     Hkv = _kv_heads(q, k)
@@ -256,7 +257,9 @@ def fa_bwd(q, k, v, o, do, lse, seg=None, scale=None, causal=True, dq=None, dk=N
         if events is None:
             st = lib.fa_bwd(*args)
         else:
-            ev = (ctypes.c_void_p * 4)(*[e or None for e in events])
+            if len(events) != 3:
+                raise ValueError("events: 3 hipEvent_t handles (or None)")
+            ev = (ctypes.c_void_p * 3)(*[e or None for e in events])
             st = lib.fa_bwd_timed(*args, ev)
     if st:
         raise FaError(st, "fa_bwd")

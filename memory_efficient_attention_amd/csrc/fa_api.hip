@@ -256,17 +256,6 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
       return FA_ERR_HIP;
   }
 
-  if (!record(events, 0, s)) return FA_ERR_HIP;
-  fa::PreParams pp{};
-  pp.o = o;
-  pp.dO = dO;
-  pp.lse = lse;
-  pp.delta = delta;
-  pp.nls = nls;
-  pp.scale = scale;
-  pp.rows = (long long)B * H * N;
-  if (fa::launch_bwd_pre(pp, dt, D, s) != hipSuccess) return FA_ERR_HIP;
-
   fa::BwdParams p{};
   p.q = q;
   p.k = k;
@@ -275,6 +264,8 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
+  p.o = o;
+  p.lse = lse;
   p.nls = nls;
   p.delta = delta;
   p.seg = seg;
@@ -286,19 +277,21 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, c
   p.c = log2e_scale(scale);
   const int cus = device_cus();
 
+  // dQ first: it also writes -D_i and -LSE / scale for its rows, which
+  // dK/dV then reads
+  if (!record(events, 0, s)) return FA_ERR_HIP;
+  p.work = seg ? (const int4*)(w + L.qwork) : nullptr;
+  p.ntiles = ntiles;
+  p.mirror = use_mirror(seg == nullptr, causal, N, nw, (long long)B * H * ntiles, cus);
+  if (fa::launch_bwd_dq(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
+
   if (!record(events, 1, s)) return FA_ERR_HIP;
   p.work = seg ? (const int4*)(w + L.kwork) : nullptr;
   p.ntiles = ntiles_kv;
   // (the kernel applies it to ungrouped heads and two-team workgroups)
   p.mirror = use_mirror(seg == nullptr, causal, N, nw_kv, (long long)B * Hkv * ntiles_kv, cus);
   if (fa::launch_bwd_dkdv(p, dt, D, causal != 0, nw_kv, s) != hipSuccess) return FA_ERR_HIP;
-
   if (!record(events, 2, s)) return FA_ERR_HIP;
-  p.work = seg ? (const int4*)(w + L.qwork) : nullptr;
-  p.ntiles = ntiles;
-  p.mirror = use_mirror(seg == nullptr, causal, N, nw, (long long)B * H * ntiles, cus);
-  if (fa::launch_bwd_dq(p, dt, D, causal != 0, nw, s) != hipSuccess) return FA_ERR_HIP;
-  if (!record(events, 3, s)) return FA_ERR_HIP;
   return FA_OK;
 }
 

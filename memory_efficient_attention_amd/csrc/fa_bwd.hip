@@ -1,4 +1,4 @@
-// Backward kernels: the D_i preprocess, dQ, and dK/dV.
+// Backward kernels: dQ (with the per-row preprocess), then dK/dV.
 //
 // The backward keeps O(N) state and recomputes the probability tiles from Q,
 // K and the saved log-sum-exp (mlx-train-perf 0.5.1 README, section
@@ -18,52 +18,13 @@
 
 namespace fa {
 
-// ---------------------------------------------------------------- preprocess
-// delta[r] = -sum_d dO[r, d] * O[r, d] (O as stored) and nls[r] = -lse[r] /
-// scale: both negated so that the dK/dV kernel can start its dP and S
-// accumulators from them (dP - D_i and S - LSE / scale come straight out of
-// the MFMAs) and the dQ kernel adds them.
-// LPR lanes share one row (LPR a power of two, so a row never straddles a
-// wave), each reading VPL 16-byte vectors of O and dO.
-template <typename T, int D>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(const PreParams p) {
-  constexpr int NV = D * (int)sizeof(T) / 16;             // 16-byte vectors per row
-  constexpr int LPR = NV & -NV;                           // largest power of two dividing NV
-  constexpr int VPL = NV / LPR;
-  constexpr int EV = 16 / (int)sizeof(T);                 // elements per vector
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = gid / LPR;
-  const int sub = (int)(gid % LPR);
-  float acc = 0.f;
-  if (row < p.rows) {
-#pragma unroll
-    for (int u = 0; u < VPL; ++u) {
-      const size_t e = (size_t)row * D + (size_t)(u * LPR + sub) * EV;
-      if constexpr (sizeof(T) == 2) {
-        const bf16x8 o = *(const bf16x8*)((const T*)p.o + e);
-        const bf16x8 g = *(const bf16x8*)((const T*)p.dO + e);
-        const f32x8 of = __builtin_convertvector(o, f32x8), gf = __builtin_convertvector(g, f32x8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc = fmaf(of[i], gf[i], acc);
-      } else {
-        const f32x4 o = *(const f32x4*)((const T*)p.o + e);
-        const f32x4 g = *(const f32x4*)((const T*)p.dO + e);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc = fmaf(o[i], g[i], acc);
-      }
-    }
-  }
-#pragma unroll
-  for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
-  if (row < p.rows && sub == 0) {
-    p.delta[row] = -acc;
-    p.nls[row] = -p.lse[row] / p.scale;
-  }
-}
-
 // ---------------------------------------------------------------- dQ
 // One workgroup = NW waves x 32 queries; walks the key tiles the query tile can
-// see.  Per tile: S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T held in registers),
+// see.  It runs first in the backward and also does the row preprocess for
+// its queries: D_i = dO_i . O_i (O as stored), and writes -D_i and -LSE_i /
+// scale, negated so that the dK/dV kernel can start its dP and S
+// accumulators from them (dP - D_i and S - LSE / scale come straight out of
+// the MFMAs).  Per tile: S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T held in registers),
 // P^T and dS^T in registers, dQ^T += K^T dS^T with K^T through the transposing
 // LDS read of the K tile.
 //
@@ -139,8 +100,24 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
     qf[ks] = gfrag_row<T, D>(gq, qc, 2 * ks + h);
     dof[ks] = gfrag_row<T, D>(gdo, qc, 2 * ks + h);
   }
-  const float nlse2 = p.c * p.nls[(size_t)bh * N + qc];   // -LSE log2(e)
-  const float ndlt = p.delta[(size_t)bh * N + qc];   // -D_i
+  // D_i from the lane's half of the row (the same 8-element chunks as its dO
+  // fragments) and the other half's lane
+  const T* go = (const T*)p.o + off;
+  float dsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const frag_t<T> of = gfrag_row<T, D>(go, qc, 2 * ks + h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum = fmaf((float)of[e], (float)dof[ks][e], dsum);
+  }
+  dsum += other_half(dsum);
+  const float nls = -p.lse[(size_t)bh * N + qc] / p.scale;
+  const float nlse2 = p.c * nls;   // -LSE log2(e)
+  const float ndlt = -dsum;        // -D_i
+  if (h == 0 && qi < N) {
+    p.nls[(size_t)bh * N + qi] = nls;
+    p.delta[(size_t)bh * N + qi] = ndlt;
+  }
   int segq = 0, segq_first = 0, segq_last = 0;
   if (packed) {
     segq = seg[qc];
@@ -418,6 +395,9 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   }
   const int rbase = L::row_base(lane);
   const int cbase = L::col_base(lane);
+  // seed value of this lane, relative to the slot's -LSE/scale vector: row
+  // col of it (lanes 0-31) or of the -D_i vector (lanes 32-63)
+  const int seed_base = (h ? OFF_DLS - OFF_NLS : 0) + 4 * col;
 
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -463,7 +443,6 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     const FA_LDS char* Qs = smem + slot * TILE;
     const FA_LDS char* dOs = smem + OFF_DO + slot * TILE;
     const FA_LDS float* nls = (const FA_LDS float*)(smem + OFF_NLS + slot * VEC);
-    const FA_LDS float* dls = (const FA_LDS float*)(smem + OFF_DLS + slot * VEC);
     const FA_LDS int* sqs = (const FA_LDS int*)(smem + OFF_SEG + buf * VEC);
     const int qtb = qt_lo + (it % nqs) * QSUB;
 #pragma unroll
@@ -486,20 +465,15 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
 
     // S - LSE / scale = Q K^T - LSE / scale and dP - D = dO V^T - D, block by
     // block: the accumulators start from the preprocess's negated per-row
-    // values, so the MFMAs deliver both differences directly.
+    // values, so the MFMAs deliver both differences directly.  The start
+    // values come from one seeding MFMA (seed_rows): lane col reads -LSE/scale
+    // of query row col (lanes 0-31) or -D_i of it (lanes 32-63), 4 bytes a
+    // lane, where broadcasting the 16 rows a lane's accumulator spans would
+    // read 128 bytes a lane from LDS per tile.
     f32x16 sacc[QB], dpacc[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 nl = *(const FA_LDS f32x4*)(nls + rs + 32 * qb + 8 * j + 4 * h);
-        const f32x4 nd = *(const FA_LDS f32x4*)(dls + rs + 32 * qb + 8 * j + 4 * h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sacc[qb][4 * j + i] = nl[i];
-          dpacc[qb][4 * j + i] = nd[i];
-        }
-      }
+      seed_rows(sacc[qb], dpacc[qb], *(const FA_LDS float*)((const FA_LDS char*)nls + seed_base + (rs + 32 * qb) * 4));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         mma(sacc[qb], frag_row<T, D>(Qs, rbase, rs + 32 * qb, ks), kf[ks]);
@@ -603,25 +577,6 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
 }
 
 // ---------------------------------------------------------------- launchers
-template <typename T, int D>
-static hipError_t launch_pre_t(const PreParams& p, hipStream_t s) {
-  constexpr int NV = D * (int)sizeof(T) / 16;
-  constexpr int LPR = NV & -NV;
-  const long long threads = p.rows * LPR;
-  const long long blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_pre(const PreParams& p, int dtype, int D, hipStream_t s) {
-  if (dtype == 0) {
-    if (D == 128) return launch_pre_t<bf16, 128>(p, s);
-    return D == 96 ? launch_pre_t<bf16, 96>(p, s) : launch_pre_t<bf16, 64>(p, s);
-  }
-  if (D == 128) return launch_pre_t<float, 128>(p, s);
-  return D == 96 ? launch_pre_t<float, 96>(p, s) : launch_pre_t<float, 64>(p, s);
-}
-
 hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s) {
   return dispatch(dtype, D, causal, nw, [&](auto t, auto d, auto c, auto w) {
     using T = typename decltype(t)::type;

@@ -24,6 +24,7 @@ typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -46,6 +47,19 @@ __device__ __forceinline__ void mma(f32x16& acc, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mma(f32x16& acc, f32x8 a, f32x8 b) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
+}
+
+// Two accumulators seeded with per-row values in one instruction: the
+// two-block fp32 MFMA (v_mfma_f32_32x32x1_2b_f32) forms, per block b, the
+// outer product of a 32-row column (lane 32b + i holds row i) with a 32-wide
+// row, into registers 16b .. 16b + 15 in the accumulator layout above.  With
+// the row all ones, lane i < 32 passing x_i and lane 32 + i passing y_i,
+// block 0 holds x_i in every column of row i and block 1 holds y_i: each lane
+// needs only its own row's value, not the 16 rows its accumulator spans.
+__device__ __forceinline__ void seed_rows(f32x16& a, f32x16& b, float v) {
+  const f32x32 r = __builtin_amdgcn_mfma_f32_32x32x1f32(v, 1.0f, f32x32{}, 0, 0, 0);
+  a = __builtin_shufflevector(r, r, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+  b = __builtin_shufflevector(r, r, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31);
 }
 
 // acc[8*kc .. 8*kc+7] as a B fragment (round to nearest even for bf16).

@@ -129,8 +129,10 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  const float* nls;      // -LSE / scale (B, H, N)
-  const float* delta;    // -D_i = -dO_i . O_i (B, H, N)
+  const void* o;         // the forward's output (dQ: D_i = dO_i . O_i)
+  const float* lse;      // the forward's log-sum-exp (dQ)
+  float* nls;            // -LSE / scale (B, H, N): written by dQ, read by dK/dV
+  float* delta;          // -D_i = -dO_i . O_i (B, H, N): written by dQ, read by dK/dV
   const int32_t* seg;
   // packed only, longest first: dQ {b, query tile, first, last key tile};
   // dK/dV {b, key tile, first, last query tile}; workgroup w runs head
@@ -152,16 +154,6 @@ __device__ __forceinline__ int mirror_block(int t, int w, int nw, int nt) {
   const int half = nw / 2, x = t * half + w % half;
   return w < half ? x : nt * nw - 1 - x;
 }
-
-struct PreParams {
-  const void* o;
-  const void* dO;
-  const float* lse;
-  float* delta;
-  float* nls;
-  float scale;
-  long long rows;
-};
 
 // Fused linear cross-entropy (bf16 H (N, D), W (V, D)).
 struct LceParams {
@@ -186,7 +178,6 @@ hipError_t launch_lce_bwd(const LceParams& p, int vc, hipStream_t s, void* const
 // Launchers (defined next to their kernels).  dtype: 0 bf16, 1 fp32; nw:
 // waves per workgroup, WAVES_DENSE or WAVES_PACKED.
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s);
-hipError_t launch_bwd_pre(const PreParams& p, int dtype, int D, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s);
 
