@@ -464,8 +464,8 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
     if (skip) continue;
 
     // S - LSE / scale = Q K^T - LSE / scale and dP - D = dO V^T - D, block by
-    // block: the accumulators start from the preprocess's negated per-row
-    // values, so the MFMAs deliver both differences directly.  The start
+    // block: the accumulators start from the negated per-row values dQ
+    // wrote, so the MFMAs deliver both differences directly.  The start
     // values come from one seeding MFMA (seed_rows): lane col reads -LSE/scale
     // of query row col (lanes 0-31) or -D_i of it (lanes 32-63), 4 bytes a
     // lane, where broadcasting the 16 rows a lane's accumulator spans would
@@ -593,9 +593,12 @@ hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int 
 }
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, int nw, hipStream_t s) {
-  // grouped heads, dense bf16, 4 key waves and an even group: two teams
+  // grouped heads, bf16, 4 key waves and an even group: two teams, for
+  // dense and packed calls alike, so that a group's dK/dV sums its heads in
+  // the same order either way and a single-segment packed call keeps the
+  // causal call's bits
   if constexpr (FA_KV_TEAMS != 0) {
-    if (nw == 4 && p.G > 1 && p.G % 2 == 0 && dtype == 0 && p.seg == nullptr) {
+    if (nw == 4 && p.G > 1 && p.G % 2 == 0 && dtype == 0) {
       const long long total = (long long)p.B * (p.H / p.G) * p.ntiles;
       auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(8 * 64), 0, s, p);

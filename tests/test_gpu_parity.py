@@ -343,6 +343,22 @@ def test_single_segment_bitwise_equals_causal_mirrored(H, N):
         assert bool((packed[n] == causal[n]).all()), f"{n}: single-segment packed != causal"
 
 
+@pytest.mark.parametrize("H,Hkv,N,D", [(8, 2, 1024, 128), (8, 4, 768, 96), (6, 2, 512, 64), (32, 8, 2048, 128)])
+def test_single_segment_bitwise_equals_causal_grouped(H, Hkv, N, D):
+    """Grouped-query heads: a single-segment packed call gives the causal
+    call's bits too.  Group sizes 4 and 2 take the two-team dK/dV kernel in
+    both calls (dense ones with mirrored key blocks at one round), the group
+    of 3 the one-team kernel."""
+    w = workloads.get("gqa_8k").with_(H=H, hkv=Hkv, N=N, D=D)
+    say(f"B1 H{H} Hkv{Hkv} N{N} D{D} bf16 as one segment and as plain causal")
+    t = w.tensors()
+    seg = np.zeros((w.B, w.N), dtype=np.int32)
+    packed = run_gpu(t, seg, w.dtype, w.scale, True)
+    causal = run_gpu(t, None, w.dtype, w.scale, True)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert bool((packed[n] == causal[n]).all()), f"{n}: single-segment packed != causal"
+
+
 def test_packed_long_documents_64k():
     w = workloads.get("packed_long_64k")
     say(f"workload {w.name}: {w.note}")
