@@ -86,12 +86,17 @@ typedef enum fa_dtype {
 
 /*
  * Bytes of workspace fa_fwd (for_bwd = 0) or fa_bwd (for_bwd = 1) needs for
- * this shape.  O(B*H*N): 256 bytes of flags, plus for the backward two fp32
- * (B, H, N) arrays (the row sums D_i = dO_i . O_i and LSE / scale, both
- * stored negated), plus
- * with has_seg two per-tile range tables of B * ceil(N/32) int32 pairs and
- * two longest-first work lists of B * ceil(N/32) int32 quadruples.
- * Returns 0 for shapes fa_fwd / fa_bwd would refuse.
+ * this shape.  The method keeps O(N) state per head (mlx-train-perf 0.5.1
+ * README, "Flash-attention training path": the forward saves only the
+ * output and the log-sum-exp, and the backward recomputes tiles from them),
+ * so the workspace is O(B*H*N): 256 bytes of flags, plus
+ * for the backward two fp32 (B, H, N) arrays (the row sums
+ * D_i = dO_i . O_i and LSE / scale, both stored negated, written by the dQ
+ * kernel for dK/dV), plus with has_seg two per-tile range tables of
+ * B * ceil(N/32) int32 pairs and two longest-first work lists of
+ * B * ceil(N/32) int32 quadruples (the packed schedule: changelog, "Added",
+ * cross-segment block skipping).  Never the (N, N) scores or mask.
+ * Returns 0 for shapes fa_fwd / fa_bwd would refuse.  Makes no HIP call.
  */
 size_t fa_workspace_bytes(int B, int H, int N, int D, int has_seg, int for_bwd);
 
@@ -173,9 +178,15 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
                          void* stream);
 
 /*
- * Host-side precondition check of a HOST copy of seg: FA_OK when every row is
- * non-decreasing, FA_ERR_SEG otherwise, FA_ERR_NULL / FA_ERR_SHAPE for bad
- * arguments.  Makes no HIP call.
+ * Host-side precondition check of a HOST copy of seg (B, N int32, row-major):
+ * FA_OK when every row is non-decreasing, i.e. every segment is one
+ * contiguous run of tokens, the form sequence packing produces (README,
+ * "Sequence packing": short sequences concatenated into fixed-length rows,
+ * a token attending only inside its own sequence) and the one the kernels'
+ * tile ranges assume; FA_ERR_SEG otherwise, FA_ERR_NULL / FA_ERR_SHAPE for bad
+ * arguments.  A refusal "naming the reason" rather than a silent wrong
+ * answer (README, "If you maintain a trainer").  Reads B * N ints, makes no
+ * HIP call; the caller keeps ownership of host_seg.
  */
 fa_status fa_check_seg(const int32_t* host_seg, int B, int N);
 

@@ -53,8 +53,9 @@ def build(verbose: bool = False, jobs: int | None = None, out: str | None = None
           extra_flags: tuple[str, ...] = ()) -> str:
     """Compile every HIP source for gfx950 and link libfa.so; returns its path.
 
-    ``out``/``defines``/``build_dir`` build a tuning variant elsewhere (e.g.
-    defines=("FA_QRY_TILE=64",)); the default builds the package library."""
+    ``out``/``defines``/``build_dir`` build the library elsewhere (with extra
+    preprocessor definitions if given); the default builds the package
+    library."""
     hipcc = _hipcc()
     bdir = build_dir or BUILD_DIR
     lib_path = out or LIB_PATH

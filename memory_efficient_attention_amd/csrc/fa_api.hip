@@ -419,8 +419,7 @@ FA_API fa_status fa_lce_bwd(const void* h, const void* w, const int32_t* targets
   p.N = N;
   p.V = V;
   p.D = D;
-  return fa::launch_lce_bwd(p, FA_LCE_VOCAB_CHUNK, (hipStream_t)stream, nullptr) == hipSuccess ? FA_OK
-                                                                                             : FA_ERR_HIP;
+  return fa::launch_lce_bwd(p, FA_LCE_VOCAB_CHUNK, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 FA_API fa_status fa_check_seg(const int32_t* host_seg, int B, int N) {
@@ -439,7 +438,7 @@ FA_API const char* fa_status_string(fa_status status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H or N out of range";
-    case FA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case FA_ERR_HEAD_DIM: return "head_dim must be 64, 96 or 128";
     case FA_ERR_DTYPE: return "dtype must be bf16 or fp32";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_workspace_bytes()";
     case FA_ERR_ALIGN: return "pointer misaligned (tensors 16 B, lse/seg 4 B, workspace 256 B)";

@@ -32,7 +32,7 @@ namespace fa {
 // walked one after the other with the same registers, so a wave does twice
 // the MFMAs per barrier; the MFMA order on every accumulator is unchanged.
 template <typename T, int D, bool CAUSAL, int NW, int KSUB = 1>
-__global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(NW * 64, WAVES_PER_EU) dq_kernel(const BwdParams p) {
   constexpr int BM = NW * 32, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
   static_assert(KSUB == 1 || (KSUB == 2 && NW == 8 && sizeof(T) == 2), "two-tile slots: 8-wave bf16");
@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
   using StK = Stager<T, SR, D, NW, true>;
   using StV = Stager<T, SR, D, NW, false>;
   constexpr int TK = LK::bytes(SR), TV = LV::bytes(SR);
-  constexpr int S = sizeof(T) == 2 ? stages_for(FA_DQ_STAGES, TK + TV + SR * 4, NW) : 2;
+  constexpr int S = sizeof(T) == 2 ? stages_for(STAGES, TK + TV + SR * 4, NW) : 2;
   static_assert(S >= 2 && S * (TK + TV + SR * 4) <= LDS_PER_CU, "K/V stages must fit in LDS");
   constexpr int LPT = (StK::NINST + StV::NINST) / NW;
   // layout: K[S] | V[S] | seg[S]
@@ -273,7 +273,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dq_kernel(const BwdP
 // twice the MFMAs per barrier.  The order of the MFMAs on every accumulator
 // is unchanged.
 template <typename T, int D, bool CAUSAL, int NW, int TEAMS = 1, int QSUB = 1>
-__global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(NW * 64, WAVES_PER_EU) dkdv_kernel(const BwdParams p) {
   constexpr int KW = NW / TEAMS;   // waves along the keys
   constexpr int BNK = KW * 32, BMQ = QRY_TILE;
   constexpr int KS = D / 16, DB = D / 32, QB = BMQ / 32;
@@ -283,7 +283,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) dkdv_kernel(const Bw
   constexpr int TILE = L::bytes(SR);
   constexpr int VEC = SR * 4;
   constexpr int PER_STAGE = TEAMS * (2 * TILE + 2 * VEC) + VEC;
-  constexpr int S = sizeof(T) == 2 ? stages_for(FA_DKV_STAGES, PER_STAGE, NW) : 2;
+  constexpr int S = sizeof(T) == 2 ? stages_for(STAGES, PER_STAGE, NW) : 2;
   static_assert(S >= 2 && S * PER_STAGE <= LDS_PER_CU, "Q/dO stages must fit in LDS");
   static_assert(TEAMS == 1 || (TEAMS == 2 && sizeof(T) == 2 && NW == 8), "teams: bf16, 8 waves");
   static_assert(TEAMS == 1 || S * PER_STAGE >= KW * 32 * D * 4, "team reduction reuses the ring");
@@ -583,7 +583,7 @@ hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, bool causal, int 
     constexpr int DD = decltype(d)::value, NW = decltype(w)::value;
     constexpr bool C = decltype(c)::value;
     const long long total = (long long)p.B * p.H * p.ntiles;
-    constexpr int KS2 = (NW == 8 && sizeof(T) == 2) ? FA_KSUB : 1;
+    constexpr int KS2 = (NW == 8 && sizeof(T) == 2) ? KSUB_DENSE : 1;
     if (KS2 > 1 && p.seg == nullptr)
       hipLaunchKernelGGL((dq_kernel<T, DD, C, NW, KS2>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
     else
@@ -597,17 +597,15 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, in
   // dense and packed calls alike, so that a group's dK/dV sums its heads in
   // the same order either way and a single-segment packed call keeps the
   // causal call's bits
-  if constexpr (FA_KV_TEAMS != 0) {
-    if (nw == 4 && p.G > 1 && p.G % 2 == 0 && dtype == 0) {
-      const long long total = (long long)p.B * (p.H / p.G) * p.ntiles;
-      auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(8 * 64), 0, s, p);
-        return hipGetLastError();
-      };
-      if (D == 128) return causal ? go(dkdv_kernel<bf16, 128, true, 8, 2>) : go(dkdv_kernel<bf16, 128, false, 8, 2>);
-      if (D == 96) return causal ? go(dkdv_kernel<bf16, 96, true, 8, 2>) : go(dkdv_kernel<bf16, 96, false, 8, 2>);
-      return causal ? go(dkdv_kernel<bf16, 64, true, 8, 2>) : go(dkdv_kernel<bf16, 64, false, 8, 2>);
-    }
+  if (nw == 4 && p.G > 1 && p.G % 2 == 0 && dtype == 0) {
+    const long long total = (long long)p.B * (p.H / p.G) * p.ntiles;
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(8 * 64), 0, s, p);
+      return hipGetLastError();
+    };
+    if (D == 128) return causal ? go(dkdv_kernel<bf16, 128, true, 8, 2>) : go(dkdv_kernel<bf16, 128, false, 8, 2>);
+    if (D == 96) return causal ? go(dkdv_kernel<bf16, 96, true, 8, 2>) : go(dkdv_kernel<bf16, 96, false, 8, 2>);
+    return causal ? go(dkdv_kernel<bf16, 64, true, 8, 2>) : go(dkdv_kernel<bf16, 64, false, 8, 2>);
   }
   return dispatch(dtype, D, causal, nw, [&](auto t, auto d, auto c, auto w) {
     using T = typename decltype(t)::type;
@@ -616,7 +614,7 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int dtype, int D, bool causal, in
     const long long total = (long long)p.B * (p.H / p.G) * p.ntiles;
     // 8-wave dK/dV workgroups are dense multi-head ones (packed and grouped
     // calls use 4): two query tiles per ring slot for bf16
-    constexpr int QS = (NW == 8 && sizeof(T) == 2) ? FA_DKV_QSUB : 1;
+    constexpr int QS = (NW == 8 && sizeof(T) == 2) ? QSUB_DENSE : 1;
     if (QS > 1 && p.seg == nullptr)
       hipLaunchKernelGGL((dkdv_kernel<T, DD, C, NW, 1, QS>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
     else

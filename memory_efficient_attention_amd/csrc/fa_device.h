@@ -141,8 +141,11 @@ struct Layout {
 // n = the loads issued for the tiles still in flight behind the one needed,
 // then a workgroup barrier.  Hidden from the compiler, these loads can only
 // make its own vmcnt waits (for register loads) stricter, never looser.
-// M0 carries the LDS address; nothing else in these kernels keeps a value in
-// M0 (checked on the built code).  The compiler cannot see the hazards of
+// M0 carries the LDS address.  M0 is a register the compiler reserves (it
+// cannot be declared clobbered), so these loads rely on nothing else in the
+// kernels reading or writing M0; tests/test_isa_m0.py checks exactly that on
+// the built code objects, so a compiler that starts using M0 fails the test
+// suite instead of corrupting loads.  The compiler cannot see the hazards of
 // these instructions, so each waits 5 states after its M0 write, which also
 // covers an SGPR operand (descriptor, address) just written by a VALU op.
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* g, int bytes) {

@@ -31,7 +31,7 @@ namespace fa {
 // the slot body).  Every operation on every row happens in the same order as
 // with one tile per slot.
 template <typename T, int D, bool CAUSAL, int NW, int KSUB = 1>
-__global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const FwdParams p) {
+__global__ void __launch_bounds__(NW * 64, WAVES_PER_EU) fwd_kernel(const FwdParams p) {
   constexpr int BM = NW * 32, BN = KEY_TILE;
   constexpr int KS = D / 16, DB = D / 32, KB = BN / 32;
   static_assert(KSUB == 1 || (KSUB == 2 && NW == 8 && sizeof(T) == 2), "two-tile slots: 8-wave bf16");
@@ -42,7 +42,7 @@ __global__ void __launch_bounds__(NW * 64, FA_WAVES_PER_EU) fwd_kernel(const Fwd
   using StK = Stager<T, SR, D, NW, false>;
   using StV = Stager<T, SR, D, NW, true>;
   constexpr int TK = LK::bytes(SR), TV = LV::bytes(SR);
-  constexpr int S = sizeof(T) == 2 ? stages_for(FA_FWD_STAGES, TK + TV + SR * 4, NW) : 2;
+  constexpr int S = sizeof(T) == 2 ? stages_for(STAGES, TK + TV + SR * 4, NW) : 2;
   static_assert(S >= 2 && S * (TK + TV + SR * 4) <= LDS_PER_CU, "K/V stages must fit in LDS");
   constexpr int LPT = (StK::NINST + StV::NINST) / NW;   // loads per wave per slot, at least
   // layout: K[S] | V[S] | seg[S]
@@ -447,7 +447,7 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, int nw,
     constexpr bool C = decltype(c)::value;
     const long long total = (long long)p.B * p.H * p.nqt;
     // 8-wave bf16 workgroups of dense calls take two key tiles per slot
-    constexpr int KS2 = (NW == 8 && sizeof(T) == 2) ? FA_KSUB : 1;
+    constexpr int KS2 = (NW == 8 && sizeof(T) == 2) ? KSUB_DENSE : 1;
     if (KS2 > 1 && p.seg == nullptr)
       hipLaunchKernelGGL((fwd_kernel<T, DD, C, NW, KS2>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
     else

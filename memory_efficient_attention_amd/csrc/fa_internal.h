@@ -14,60 +14,28 @@ namespace fa {
 // changes a result bit.  Dense (causal or full) calls use WAVES_DENSE waves,
 // whose one staged tile feeds the most waves; packed calls use WAVES_PACKED,
 // whose smaller workgroups track short segments more closely and keep two
-// workgroups per CU in flight.  Overridable at build time
-// (-DFA_<NAME>=value).
-#ifndef FA_WAVES_DENSE
-#define FA_WAVES_DENSE 8
-#endif
-#ifndef FA_WAVES_PACKED
-#define FA_WAVES_PACKED 4
-#endif
-#ifndef FA_KEY_TILE
-#define FA_KEY_TILE 64
-#endif
-#ifndef FA_QRY_TILE
-#define FA_QRY_TILE 32
-#endif
-// Waves per SIMD the kernels are compiled for (their register budget is
-// 512 / this per lane).
-#ifndef FA_WAVES_PER_EU
-#define FA_WAVES_PER_EU 2
-#endif
-// Load pipeline depth: each kernel keeps up to STAGES - 1 tiles staged ahead
-// of the one it computes on, as far as its LDS share allows.  Measured on
-// MI355X, rings deeper than two stages gain nothing here (within 1 %), and
-// the dK/dV kernel, which runs at the 256-register limit, spills with three;
-// fp32 tiles (small shapes only) always use two stages and full waits.
-// Two-team dK/dV workgroups for grouped-query heads (see dkdv_kernel); 0
-// turns them off.
-#ifndef FA_KV_TEAMS
-#define FA_KV_TEAMS 1
-#endif
-// Key tiles per ring slot in 8-wave bf16 forward and dQ workgroups (1 or 2).
-#ifndef FA_KSUB
-#define FA_KSUB 2
-#endif
-// Query tiles per ring slot in dense multi-head 8-wave dK/dV (1 or 2).
-#ifndef FA_DKV_QSUB
-#define FA_DKV_QSUB 2
-#endif
-#ifndef FA_FWD_STAGES
-#define FA_FWD_STAGES 2
-#endif
-#ifndef FA_DQ_STAGES
-#define FA_DQ_STAGES 2
-#endif
-#ifndef FA_DKV_STAGES
-#define FA_DKV_STAGES 2
-#endif
-constexpr int WAVES_DENSE = FA_WAVES_DENSE;
-constexpr int WAVES_PACKED = FA_WAVES_PACKED;
-constexpr int KEY_TILE = FA_KEY_TILE;
-constexpr int QRY_TILE = FA_QRY_TILE;
+// workgroups per CU in flight.
+constexpr int WAVES_DENSE = 8;
+constexpr int WAVES_PACKED = 4;
+constexpr int KEY_TILE = 64;
+constexpr int QRY_TILE = 32;
+// Waves per SIMD the attention kernels are compiled for (their register
+// budget is 512 / this per lane).
+constexpr int WAVES_PER_EU = 2;
+// Load pipeline depth of every attention kernel: one tile staged ahead of
+// the one in use.  Measured on MI355X, deeper rings gain nothing here
+// (within 1 %), and the dK/dV kernel, at the 256-register limit, spills
+// with three stages.
+constexpr int STAGES = 2;
+// Two tiles per ring slot in the 8-wave bf16 kernels of dense calls: key
+// tiles in the forward and dQ (KSUB), query tiles in multi-head dK/dV
+// (QSUB).
+constexpr int KSUB_DENSE = 2;
+constexpr int QSUB_DENSE = 2;
 constexpr int LDS_PER_CU = 163840;
-constexpr int WAVES_PER_CU = 4 * FA_WAVES_PER_EU;
+constexpr int WAVES_PER_CU = 4 * WAVES_PER_EU;
 
-// Tile configuration by shape class: waves per workgroup of the forward and
+// Tile configuration by call mode: waves per workgroup of the forward and
 // dQ (nw_q) and of dK/dV (nw_kv).  Where the mlx-train-perf README ("Turning
 // it on", "Training packed") calibrates its kernels with a host-synced timing
 // probe cached per batch size and sequence bucket, this is a fixed table,
@@ -77,9 +45,14 @@ constexpr int WAVES_PER_CU = 4 * FA_WAVES_PER_EU;
 //   dense (causal or full), multi-head: 8 / 8 waves
 //   packed:                             4 / 4 waves (short segments, many
 //                                       small workgroups per CU)
-//   dense, grouped-query heads:         8 / 4 waves (dK/dV has H/Hkv times
-//                                       fewer workgroups; two per CU pair heavy
-//                                       and light causal key tiles)
+//   dense, grouped-query heads:         8 / 4 waves (two-team dK/dV for even
+//                                       groups: 8-wave workgroups of 128 keys)
+// The key is the mode, not the size: A/B runs of 4- against 8-wave
+// workgroups for every class at several sizes (2k to 64k rows, head_dim 64
+// to 128) found no size at which the other choice wins by more than noise,
+// and a size-keyed choice of key-tile length is ruled out because the host
+// cannot tell a packed call's segment lengths (they are device data) while a
+// single-segment packed call must keep the causal call's tile order.
 struct TileConfig {
   int nw_q, nw_kv;
 };
@@ -173,7 +146,7 @@ struct LceParams {
   int N, V, D;
 };
 hipError_t launch_lce_fwd(const LceParams& p, hipStream_t s);
-hipError_t launch_lce_bwd(const LceParams& p, int vc, hipStream_t s, void* const* events);
+hipError_t launch_lce_bwd(const LceParams& p, int vc, hipStream_t s);
 
 // Launchers (defined next to their kernels).  dtype: 0 bf16, 1 fp32; nw:
 // waves per workgroup, WAVES_DENSE or WAVES_PACKED.

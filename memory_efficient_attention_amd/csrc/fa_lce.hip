@@ -37,26 +37,18 @@ namespace fa {
 
 namespace {
 
-// Per-wave block WM x WN (MB x NB MFMA tiles of 32 x 32).  64 x 128 runs 8
-// waves at 2 per SIMD; 128 x 128 runs 4 waves at 1 per SIMD, with twice the
-// registers and 2/3 of the LDS reads per MFMA.
-#ifndef FA_LCE_WAVE_M
-#define FA_LCE_WAVE_M 64
-#endif
-#ifndef FA_LCE_STAGES
-#define FA_LCE_STAGES 2
-#endif
-#ifndef FA_LCE_TK
-#define FA_LCE_TK 64
-#endif
-constexpr int TM = 256, TN = 256, TK = FA_LCE_TK;   // contraction slice per stage
-constexpr int WM = FA_LCE_WAVE_M, WN = 128;
+// Per-wave block WM x WN (MB x NB MFMA tiles of 32 x 32): 64 x 128, 8 waves
+// at 2 per SIMD.  (128 x 128 blocks at one wave per SIMD, with 2/3 of the
+// LDS reads per MFMA, measured 4 % slower.)  The contraction is staged in
+// slices of TK = 64 through a ring of 2 stages.
+constexpr int TM = 256, TN = 256, TK = 64;   // contraction slice per stage
+constexpr int WM = 64, WN = 128;
 constexpr int MB = WM / 32, NB = WN / 32;
 constexpr int WAVES_M = TM / WM, WAVES_N = TN / WN, NWV = WAVES_M * WAVES_N;
 constexpr int WPE = NWV >= 8 ? 2 : 1;          // waves per SIMD the registers allow
-constexpr int STAGES = FA_LCE_STAGES;
+constexpr int LCE_STAGES = 2;
 static_assert(WM == 64 || WM == 128, "per-wave block");
-static_assert(STAGES >= 2 && STAGES <= 4, "stage ring");
+static_assert(LCE_STAGES >= 2 && LCE_STAGES <= 4, "stage ring");
 static_assert(TK == 32 || TK == 64, "contraction slice");
 using LRow = Layout<bf16, TK, false>;     // 256 rows x TK elements
 using LCol = Layout<bf16, TM, true>;      // TK rows x 256 elements (transposed reads)
@@ -96,7 +88,7 @@ __device__ __forceinline__ int dz_pos(int j) { return (j & ~12) | ((j & 4) << 1)
 // The GEMM core.  A (M x K) and B (K x N) are staged per K-slice by
 // stage_a(tile, k0) / stage_b(tile, k0) and read as `OA` / `OB` operands;
 // acc[mb][nb] is the wave's MB x NB block of 32 x 32 tiles.  The ring holds
-// STAGES K-slices; slice s + STAGES - 1 is issued once slice s - 1's buffer
+// LCE_STAGES K-slices; slice s + LCE_STAGES - 1 is issued once slice s - 1's buffer
 // is free.  Every slice ends at a workgroup barrier, where both waves of a
 // SIMD stop together; so the MFMAs of each slice's last 16-wide step are
 // issued only after the next barrier, where they keep the matrix unit busy
@@ -139,19 +131,19 @@ __device__ __forceinline__ void gemm_tile(FA_LDS char* smem, int nk, SA&& stage_
       for (int nb = 0; nb < NB; ++nb) mma(acc[mb][nb], a[mb], b[nb]);
   };
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
+  for (int s = 0; s < LCE_STAGES - 1; ++s)
     if (s < nk) stage(s, s);
   bf16x8 pa[MB], pb[NB];   // the previous slice's last step, not yet multiplied
   int buf = 0;
   for (int s = 0; s < nk; ++s) {
-    // slices s + 1 .. s + STAGES - 2 may stay in flight
-    wait_tiles<LPT, STAGES - 2>(min(nk - 1 - s, STAGES - 2));
+    // slices s + 1 .. s + LCE_STAGES - 2 may stay in flight
+    wait_tiles<LPT, LCE_STAGES - 2>(min(nk - 1 - s, LCE_STAGES - 2));
     lds_drain();   // pa / pb were read from the buffer this barrier frees
     __syncthreads();
-    if (s + STAGES - 1 < nk) stage(s + STAGES - 1, buf == 0 ? STAGES - 1 : buf - 1);
+    if (s + LCE_STAGES - 1 < nk) stage(s + LCE_STAGES - 1, buf == 0 ? LCE_STAGES - 1 : buf - 1);
     const FA_LDS char* ta = smem + buf * 2 * TILE_MAX;
     const FA_LDS char* tb = ta + TILE_MAX;
-    buf = buf + 1 == STAGES ? 0 : buf + 1;
+    buf = buf + 1 == LCE_STAGES ? 0 : buf + 1;
     bf16x8 a[MB], b[NB];
     read(ta, tb, 0, a, b);
     if (s > 0) mmas(pa, pb);
@@ -182,7 +174,7 @@ __device__ __forceinline__ void gemm_tile(FA_LDS char* smem, int nk, SA&& stage_
 // and exp-sum (log2 domain) into part[vt][token], and the target logit where
 // the tile holds it.
 __global__ void __launch_bounds__(NWV * 64, WPE) lce_fwd_kernel(const LceParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGES * TILE_MAX];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * LCE_STAGES * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -292,7 +284,7 @@ __global__ void __launch_bounds__(RED_WAVES * 64) lce_reduce_kernel(const LcePar
 // dZ = g (exp(Z - LSE) - [v = t]) stored as bf16 to dz[token][dz_pos(v - c0)]
 // (zeros past V, so the following products see none of those columns).
 __global__ void __launch_bounds__(NWV * 64, WPE) lce_dz_kernel(const LceParams p, int c0, int vc, int kvalid) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGES * TILE_MAX];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * LCE_STAGES * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -343,7 +335,7 @@ __global__ void __launch_bounds__(NWV * 64, WPE) lce_dz_kernel(const LceParams p
 // accumulator), 2 middle (accumulate), 3 last (accumulate and write dh).
 __global__ void __launch_bounds__(NWV * 64, WPE) lce_dh_kernel(const LceParams p, int c0, int vc,
                                                               int kvalid, int mode) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGES * TILE_MAX];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * LCE_STAGES * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -387,7 +379,7 @@ __global__ void __launch_bounds__(NWV * 64, WPE) lce_dh_kernel(const LceParams p
 // dW^T (D x VC) = H^T dZ over all tokens for the chunk's vocabulary rows: one
 // workgroup per (hidden tile, vocabulary tile of the chunk).
 __global__ void __launch_bounds__(NWV * 64, WPE) lce_dw_kernel(const LceParams p, int c0, int vc, int kvalid) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGES * TILE_MAX];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * LCE_STAGES * TILE_MAX];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -436,7 +428,7 @@ hipError_t launch_lce_fwd(const LceParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_lce_bwd(const LceParams& p, int vc, hipStream_t s, void* const* events) {
+hipError_t launch_lce_bwd(const LceParams& p, int vc, hipStream_t s) {
   const int ntt = (p.N + TN - 1) / TN, ndt = p.D / TM;
   const int nchunks = (p.V + vc - 1) / vc;
   for (int c = 0; c < nchunks; ++c) {
@@ -446,7 +438,6 @@ hipError_t launch_lce_bwd(const LceParams& p, int vc, hipStream_t s, void* const
     // written as zeros, and dh reads no further than that tile)
     const int kvalid = min(vc, p.V - c0);
     const int nvt = (kvalid + TM - 1) / TM;
-    if (events && events[0] && c == 0) (void)hipEventRecord((hipEvent_t)events[0], s);
     hipLaunchKernelGGL(lce_dz_kernel, dim3((unsigned)(nvt * ntt)), dim3(NWV * 64), 0, s, p, c0, vc, kvalid);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     const int mode = nchunks == 1 ? 0 : (c == 0 ? 1 : (c + 1 == nchunks ? 3 : 2));

@@ -188,6 +188,8 @@ def test_status_strings(lib):
         seen.add(txt)
     assert len(seen) == 12
     assert lib.fa_status_string(1234).decode() == "unknown status"
+    # the head-dim refusal names every supported head dim
+    assert lib.fa_status_string(FA_ERR_HEAD_DIM).decode() == "head_dim must be 64, 96 or 128"
 
 
 # ---------------------------------------------------------------- linear cross-entropy
