@@ -331,7 +331,7 @@ def headline(args):
         "pct_bf16_peak": round(100.0 * res["tflops"] / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in res["stage_ms"].items()},
         "roofline": roofline(w, res),
-        "n8k": eight_k(args.steps, args.warmup) if w.name == DEFAULT_WORKLOAD else None,
+        "n8k": eight_k(args.steps, args.warmup) if w.name == DEFAULT_WORKLOAD and not args.no_8k else None,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -495,8 +495,10 @@ def ingest_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload
 
 def summarize_trace(path, warmup):
     """Per-kernel launch statistics from a rocprofv3 --kernel-trace run of
-    this script: the first `warmup` dispatches of each kernel (the untimed
-    warm-up steps) are dropped, the rest summarised (ms)."""
+    this script, one row per (kernel, grid size) so that the headline
+    workload and the 8k ones stay apart: the first `warmup` dispatches of
+    each row (the untimed warm-up steps) are dropped, the rest summarised
+    (ms)."""
     import csv
     import glob
     import statistics
@@ -508,19 +510,50 @@ def summarize_trace(path, warmup):
         with open(f) as fh:
             for r in csv.DictReader(fh):
                 name = r.get("Kernel_Name", "")
-                short = next((k for k, n in KERNEL_NAMES.items() if n in name), None)
-                if short is None:
+                if not any(n in name for n in KERNEL_NAMES.values()):
                     continue
-                per.setdefault(name, []).append((int(r["Start_Timestamp"]),
-                                                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6))
-    out = {}
-    for name, v in per.items():
+                grid = r.get("Grid_Size_X") or r.get("Grid_Size") or "?"
+                wg = r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or "?"
+                per.setdefault((name, grid, wg), []).append(
+                    (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6))
+    out = []
+    for (name, grid, wg), v in sorted(per.items(), key=lambda kv: min(t for t, _ in kv[1])):
         d = [x for _, x in sorted(v)][warmup:]
         if not d:
             continue
-        out[name] = {"calls": len(d), "avg_ms": round(statistics.fmean(d), 4),
-                     "median_ms": round(statistics.median(d), 4), "min_ms": round(min(d), 4),
-                     "max_ms": round(max(d), 4)}
+        out.append({"kernel": name, "grid_threads": grid, "workgroup": wg, "calls": len(d),
+                    "avg_ms": round(statistics.fmean(d), 4), "median_ms": round(statistics.median(d), 4),
+                    "min_ms": round(min(d), 4), "max_ms": round(max(d), 4)})
+    print(json.dumps(out, indent=1))
+
+
+def summarize_counters(path):
+    """Per (kernel, grid size) averages of every counter in the rocprofv3
+    --pmc runs under path (all dispatches)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    acc = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name", "")
+                if not any(n in name for n in KERNEL_NAMES.values()):
+                    continue
+                key = (name, r.get("Grid_Size") or r.get("Grid_Size_X") or "?")
+                d = acc.setdefault(key, {})
+                d.setdefault((r.get("Dispatch_Id"), r["Counter_Name"]), 0.0)
+                d[(r.get("Dispatch_Id"), r["Counter_Name"])] += float(r["Counter_Value"])
+    out = []
+    for (name, grid), d in sorted(acc.items()):
+        per = {}
+        for (disp, cname), v in d.items():
+            per.setdefault(cname, []).append(v)
+        out.append({"kernel": name, "grid_threads": grid,
+                    "dispatches": max(len(v) for v in per.values()),
+                    "avg": {c: sum(v) / len(v) for c, v in sorted(per.items())}})
     print(json.dumps(out, indent=1))
 
 
@@ -531,6 +564,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-8k", action="store_true", help="leave out the 8k fields (profiling runs of one shape)")
     ap.add_argument("--all", action="store_true", help="table over every workload instead of the JSON line")
     ap.add_argument("--lce", action="store_true", help="time the fused linear cross-entropy loss layer")
     ap.add_argument("--copy-calibration", action="store_true", help="plain copy of known size for counters")
@@ -539,7 +573,12 @@ def main():
                     help="write profiles/traffic.json from rocprofv3 counter runs (CPU only)")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="per-kernel statistics of a rocprofv3 kernel trace of this script, warm-up dropped")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="per-kernel averages of the counters of a rocprofv3 --pmc run of this script")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.warmup)
         return
