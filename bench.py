@@ -10,7 +10,8 @@ tensors already resident in HBM when the timed region starts.
 Beside the headline number the line carries
 * ``roofline``: the dominant kernel's algorithmic flops per launch over its
   average launch time, measured with HIP events recorded on the launch stream
-  around that kernel in every timed step; ``traffic`` is its HBM bytes per
+  around that kernel in a second pass of the same steps (the step time itself
+  is taken with events at step boundaries only); ``traffic`` is its HBM bytes per
   launch from rocprofv3 counters (profiles/traffic.json), or null when the
   kernel sources changed since the counters were taken;
 * ``cpu_baseline``: the fp64 oracle timed on this host on a bounded sample of
@@ -160,18 +161,31 @@ def run_workload(w, steps: int, warmup: int, seg_override="keep", causal=True, q
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
     for _ in range(warmup):
         step()
-    stage_ev = [[ev.new() for _ in range(5)] for _ in range(steps)]
-    t0, t1 = ev.new(), ev.new()
+    # Timed region 1, the step time: one event at each step boundary and none
+    # inside a step (an event between two kernels drains the queue, which
+    # costs the short workloads up to 0.1 ms a step).  Cold: the scratch
+    # write sits outside the step's events.
+    bounds = [[ev.new(), ev.new()] if cold else [ev.new()] for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    ev.record(t0, stream)
+    ev.record(bounds[0][-1], stream)
+    for i in range(steps):
+        if cold:
+            scratch.fill_(i & 255)
+            ev.record(bounds[i][-1], stream)
+        step()
+        ev.record(bounds[i + 1][0], stream)
+    torch.cuda.synchronize()
+    per_step = sorted(ev.ms(bounds[i][-1], bounds[i + 1][0]) for i in range(steps))
+    total_ms = sum(per_step) if cold else ev.ms(bounds[0][-1], bounds[steps][0])
+    # Timed region 2, the kernels: the same steps with events around each
+    # kernel, for the per-kernel averages (the roofline's launch durations).
+    stage_ev = [[ev.new() for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
     for i in range(steps):
         if cold:
             scratch.fill_(i & 255)
         step(stage_ev[i])
-    ev.record(t1, stream)
     torch.cuda.synchronize()
-    per_step = sorted(ev.ms(e[0], e[4]) for e in stage_ev)
-    total_ms = sum(per_step) if cold else ev.ms(t0, t1)
     stage = {k: 0.0 for k in KERNELS}
     for e in stage_ev:
         stage["fwd"] += ev.ms(e[0], e[1])
@@ -560,8 +574,8 @@ def summarize_counters(path):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-8k", action="store_true", help="leave out the 8k fields (profiling runs of one shape)")

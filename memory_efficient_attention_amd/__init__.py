@@ -373,12 +373,11 @@ def fa_lce_bwd(h, w, targets, lse, dnll, need_dw=True, workspace=None):
     return dh, dw
 
 
-def linear_cross_entropy(h, w, targets, reduction="mean"):
-    """Differentiable loss through fa_lce_fwd / fa_lce_bwd: NLL of
-    softmax(h w^T) at `targets`, reduced by "mean", "sum" or "none"."""
+def linear_cross_entropy(h, w, targets):
+    """Differentiable per-token loss through fa_lce_fwd / fa_lce_bwd: the NLL
+    of softmax(h w^T) at `targets`, an (N,) fp32 tensor.  Reducing it (mean,
+    sum) is the caller's step; its gradient reaches fa_lce_bwd per token."""
     import torch
-    if reduction not in ("mean", "sum", "none"):
-        raise ValueError(f"reduction {reduction!r}")
 
     class _Fn(torch.autograd.Function):
         @staticmethod
@@ -390,10 +389,7 @@ def linear_cross_entropy(h, w, targets, reduction="mean"):
         @staticmethod
         def backward(ctx, g):
             h_, w_, lse = ctx.saved_tensors
-            dh, dw = fa_lce_bwd(h_, w_, targets, lse, g.contiguous().float(), need_dw=ctx.needs_input_grad[1])
+            dh, dw = fa_lce_bwd(h_, w_, targets, lse, g.contiguous(), need_dw=ctx.needs_input_grad[1])
             return dh, dw
 
-    nll = _Fn.apply(h, w)
-    if reduction == "mean":
-        return nll.mean()
-    return nll.sum() if reduction == "sum" else nll
+    return _Fn.apply(h, w)
