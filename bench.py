@@ -58,14 +58,14 @@ def visible_pairs(B, H, N, seg, causal=True) -> int:
 
 
 def kernel_sources_sha() -> str:
-    """Hash of the sources the attention kernels are compiled from (the loss
-    layer's kernels and the host-side API file do not change them)."""
+    """Hash of the sources the attention kernels (forward, dQ, dK/dV) are
+    compiled from; the schedule, the loss layer and the host-side API files
+    do not change them."""
     d = os.path.join(ROOT, "memory_efficient_attention_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h")) and name not in ("fa_lce.hip", "fa_api.hip"):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in ("fa_bwd.hip", "fa_device.h", "fa_fwd.hip", "fa_internal.h"):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
