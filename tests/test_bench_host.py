@@ -72,3 +72,36 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_trace_summary_drops_warmup_per_kernel_and_grid(tmp_path, capsys):
+    """--summarize-trace keeps the headline and 8k dispatches of one kernel
+    apart by grid size and drops the first `warmup` of each."""
+    import json
+    rows = ["Kernel_Name,Grid_Size_X,Workgroup_Size_X,Start_Timestamp,End_Timestamp"]
+    t = 0
+    for grid, durs in (("1048576", [9, 9, 2, 2, 2]), ("524288", [7, 1, 1])):
+        for d in durs:
+            rows.append(f"fa::dkdv_kernel<x>,{grid},512,{t},{t + d * 1000000}")
+            t += 10 ** 8
+    (tmp_path / "a_kernel_trace.csv").write_text("\n".join(rows) + "\n")
+    bench.summarize_trace(str(tmp_path), 2)
+    out = json.loads(capsys.readouterr().out)
+    by_grid = {r["grid_threads"]: r for r in out}
+    assert by_grid["1048576"]["calls"] == 3 and by_grid["1048576"]["avg_ms"] == 2.0
+    assert by_grid["524288"]["calls"] == 1 and by_grid["524288"]["avg_ms"] == 1.0
+
+
+def test_counter_summary_averages_per_dispatch(tmp_path, capsys):
+    """--summarize-counters sums a counter's instances within a dispatch,
+    then averages over dispatches, per (kernel, grid)."""
+    import json
+    rows = ["Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value"]
+    for disp, vals in ((1, (3, 5)), (2, (4, 4))):
+        for v in vals:   # two instances (e.g. XCDs) of one counter per dispatch
+            rows.append(f"{disp},fa::dq_kernel<x>,1024,SQ_INSTS_MFMA,{v}")
+    rows.append("3,other_kernel,64,SQ_INSTS_MFMA,100")
+    (tmp_path / "p_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    bench.summarize_counters(str(tmp_path))
+    out = json.loads(capsys.readouterr().out)
+    assert len(out) == 1 and out[0]["dispatches"] == 2 and out[0]["avg"]["SQ_INSTS_MFMA"] == 8.0

@@ -66,3 +66,46 @@ def test_too_large_is_refused():
     with pytest.raises(fa.FaError) as e:
         fa.fa_bwd_noalloc(x, x, x, x, x, lse, None, 0.125, True, dq=x, dk=x, dv=x)
     assert e.value.status == fa.FA_ERR_SCRATCH
+
+
+def test_graph_capture_of_the_allocation_free_backward():
+    """The callers it is for: a dense causal step (fa_fwd needs no workspace
+    there) with fa_bwd_noalloc, captured in a HIP graph with no buffer but
+    the inputs and outputs; every replay equals the eager step bitwise, with
+    new inputs and eager work between replays."""
+    import torch
+    import memory_efficient_attention_amd as fa
+    B, H, N, D = 1, 4, 600, 128
+    say(f"graph capture of fa_fwd + fa_bwd_noalloc B{B} H{H} N{N} D{D}")
+    g = torch.Generator(device="cuda").manual_seed(13)
+    q, k, v, do = (torch.empty(B, H, N, D, device="cuda", dtype=torch.bfloat16) for _ in range(4))
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty(B, H, N, device="cuda")
+
+    def refill():
+        for t in (q, k, v, do):
+            t.copy_(torch.randn(t.shape, device="cuda", generator=g))
+
+    def step():
+        fa.fa_fwd(q, k, v, None, None, True, out=o, lse=lse)
+        fa.fa_bwd_noalloc(q, k, v, o, do, lse, None, None, True, dq=dq, dk=dk, dv=dv)
+
+    refill()
+    step()   # code objects loaded and the array's address looked up before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        refill()
+        step()
+        torch.cuda.synchronize()
+        want = [t.clone() for t in (o, lse, dq, dk, dv)]
+        for t in (o, lse, dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, ref in zip(("o", "lse", "dq", "dk", "dv"), (o, lse, dq, dk, dv), want):
+            assert bool((got == ref).all()), f"replay {rep}: {name} differs from eager"
