@@ -122,6 +122,17 @@ def executed_flops(kernel: str, D: int, V: int) -> float:
 
 # ---------------------------------------------------------------- one workload
 
+def alg_bytes(w) -> float:
+    """Compulsory HBM bytes of one fwd + bwd step through the ABI: the
+    forward reads q, k, v and writes o, lse; the backward reads q, k, v, o,
+    dO, lse and writes dq, dk, dv.  Each (B, H, N, D) tensor once per use,
+    k and v with their Hkv heads."""
+    elt = 2 if w.dtype == "bf16" else 4
+    tq = w.B * w.H * w.N * w.D * elt
+    tkv = w.B * w.Hkv * w.N * w.D * elt
+    return 6.0 * tq + 6.0 * tkv + 2.0 * w.B * w.H * w.N * 4
+
+
 def run_workload(w, steps: int, warmup: int, seg_override="keep", causal=True, quiet=False, cold=False):
     """Time `steps` fwd+bwd steps after `warmup`.  cold: a 512 MiB scratch
     buffer is written between steps (outside the timed events), so no step
@@ -408,7 +419,8 @@ def report_all(args):
         print(f"# running {name}", file=sys.stderr, flush=True)
         r = run_workload(w, args.steps, args.warmup)
         row = dict(workload=name, ms=r["ms"], ms_median=r["ms_median"], ms_min=r["ms_min"],
-                   tflops=r["tflops"], V=r["V"], stages=r["stage_ms"])
+                   tflops=r["tflops"], V=r["V"], stages=r["stage_ms"],
+                   alg_gbs=alg_bytes(w) / (r["ms"] * 1e-3) / 1e9)
         if w.layout in ("short", "long", "single"):
             c = run_workload(w, args.steps, args.warmup, seg_override=None)
             row["causal_ms"] = c["ms"]
@@ -424,8 +436,8 @@ def report_all(args):
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in row.items()}),
               flush=True)
     print("\n| workload | ms fwd+bwd (mean) | median | min | fwd | dQ (with D_i) | dK/dV | eff. TFLOP/s | % peak | "
-          "packed speedup vs causal (visible ratio) |")
-    print("|---|---|---|---|---|---|---|---|---|---|")
+          "algorithmic GB/s | packed speedup vs causal (visible ratio) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
         s = r["stages"]
         sp = (f"{r['speedup_vs_causal']:.2f}x ({r['visible_ratio']:.2f}x) against causal {r['causal_ms']:.3f} ms "
@@ -435,7 +447,7 @@ def report_all(args):
             sp += f"; cache-cold {r['cold_ms']:.3f} ms"
         print(f"| {r['workload']} | {r['ms']:.3f} | {r['ms_median']:.3f} | {r['ms_min']:.3f} | {s['fwd']:.3f} | "
               f"{s['dq']:.3f} | {s['dkdv']:.3f} | {r['tflops']:.1f} | "
-              f"{100 * r['tflops'] / PEAK_BF16_TFLOPS:.1f} | {sp} |")
+              f"{100 * r['tflops'] / PEAK_BF16_TFLOPS:.1f} | {r['alg_gbs']:.0f} | {sp} |")
 
 
 COPY_BYTES = 1 << 30

@@ -105,3 +105,18 @@ def test_counter_summary_averages_per_dispatch(tmp_path, capsys):
     bench.summarize_counters(str(tmp_path))
     out = json.loads(capsys.readouterr().out)
     assert len(out) == 1 and out[0]["dispatches"] == 2 and out[0]["avg"]["SQ_INSTS_MFMA"] == 8.0
+
+
+def test_algorithmic_bytes_follow_the_abi():
+    """Compulsory bytes of one fwd + bwd step: every tensor the two calls
+    read or write, once per call that touches it (brute-force list)."""
+    for name in ("causal_16k", "gqa_8k", "tiny_causal_fp32", "packed_short_4k"):
+        w = workloads.get(name)
+        elt = 2 if w.dtype == "bf16" else 4
+        q = w.B * w.H * w.N * w.D * elt
+        kv = w.B * w.Hkv * w.N * w.D * elt
+        rows = w.B * w.H * w.N * 4
+        fwd = [q, kv, kv, q, rows]                      # read q k v, write o lse
+        bwd = [q, kv, kv, q, q, rows, q, kv, kv]        # read q k v o dO lse, write dq dk dv
+        assert bench.alg_bytes(w) == sum(fwd) + sum(bwd)
+    assert bench.alg_bytes(workloads.get("causal_16k")) == 1614807040
