@@ -542,6 +542,19 @@ __global__ void __launch_bounds__(NW * 64, WAVES_PER_EU) dkdv_kernel(const BwdPa
           mma(dvacc[db], frag_col<T, D>(dOs, cbase, rs + 32 * qb + 16 * kc, 32 * db), pf[kc]);
           mma(dkacc[db], frag_col<T, D>(Qs, cbase, rs + 32 * qb + 16 * kc, 32 * db), dsf[kc]);
         }
+      // bf16: each of these MFMAs takes its A fragment from two transposing
+      // LDS reads; have them issued one MFMA ahead.  Left to itself the
+      // compiler waits for each pair just before its MFMA (lgkmcnt(0) every
+      // time).  Only the issue order changes, so the results do not.
+      if constexpr (sizeof(T) == 2) {
+        constexpr int NM = DB * 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          if (i + 1 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
     }
     }
   }
