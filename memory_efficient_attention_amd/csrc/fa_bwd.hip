@@ -165,13 +165,21 @@ __global__ void __launch_bounds__(NW * 64, WAVES_PER_EU) dq_kernel(const BwdPara
     const int buf = js % S;
     wait_tiles<LPT, S - 2>(nst - 1 - js);
     __syncthreads();
-    if (js + S - 1 < nst) stage(js + S - 1, buf == 0 ? S - 1 : buf - 1);
+    // With two tiles per slot the next slot's loads go out at the second
+    // tile (see the sub loop); with one, right after the barrier.
+    const bool more = js + S - 1 < nst;
+    const int nbuf = buf == 0 ? S - 1 : buf - 1;
+    if (KSUB == 1 && more) stage(js + S - 1, nbuf);
 
     const FA_LDS char* Ks = smem + buf * TK;
     const FA_LDS char* Vs = smem + S * TK + buf * TV;
     const FA_LDS int* segs = (const FA_LDS int*)(smem + S * (TK + TV) + buf * SR * 4);
 #pragma unroll
     for (int sub = 0; sub < KSUB; ++sub) {
+    // Issued here, the loads do not crowd the first tile's fragment reads
+    // at the moment every wave leaves the barrier (measured faster); the
+    // slot they fill was released by that barrier.
+    if (KSUB == 2 && sub == 1 && more) stage(js + S - 1, nbuf);
     const int kt = kt_lo + KSUB * js + sub;
     if (kt > kt_hi) break;
     const int rs = BN * sub;   // first row of this key tile in the slot
@@ -437,7 +445,9 @@ __global__ void __launch_bounds__(NW * 64, WAVES_PER_EU) dkdv_kernel(const BwdPa
     const int buf = it % S;
     wait_tiles<LPT, S - 2>(nit - 1 - it);
     __syncthreads();
-    if (it + S - 1 < nit) stage(it + S - 1, buf == 0 ? S - 1 : buf - 1);
+    const bool more = it + S - 1 < nit;
+    const int nbuf = buf == 0 ? S - 1 : buf - 1;
+    if (QSUB == 1 && more) stage(it + S - 1, nbuf);   // two-tile slots: at the second tile
 
     const int slot = buf * TEAMS + team;
     const FA_LDS char* Qs = smem + slot * TILE;
@@ -447,6 +457,7 @@ __global__ void __launch_bounds__(NW * 64, WAVES_PER_EU) dkdv_kernel(const BwdPa
     const int qtb = qt_lo + (it % nqs) * QSUB;
 #pragma unroll
     for (int sub = 0; sub < QSUB; ++sub) {
+    if (QSUB == 2 && sub == 1 && more) stage(it + S - 1, nbuf);   // as in dQ
     const int qt = qtb + sub;
     if (qt > qt_hi) break;
     const int rs = 32 * QB * sub;   // first row of this query tile in the slot
