@@ -89,11 +89,12 @@ __device__ __forceinline__ int dz_pos(int j) { return (j & ~12) | ((j & 4) << 1)
 // stage_a(tile, k0) / stage_b(tile, k0) and read as `OA` / `OB` operands;
 // acc[mb][nb] is the wave's MB x NB block of 32 x 32 tiles.  The ring holds
 // LCE_STAGES K-slices; slice s + LCE_STAGES - 1 is issued halfway through
-// slice s, into slice s - 1's buffer (free since the barrier).  Every slice ends at a workgroup barrier, where both waves of a
-// SIMD stop together; so the MFMAs of each slice's last 16-wide step are
-// issued only after the next barrier, where they keep the matrix unit busy
-// while the new slice's first fragments come from LDS.  The order of the
-// MFMAs on each accumulator is unchanged.
+// slice s, into slice s - 1's buffer (free since the barrier).  Every slice
+// ends at a workgroup barrier, where both waves of a SIMD stop together; so
+// the MFMAs of each slice's last 16-wide step are issued only after the next
+// barrier, where they keep the matrix unit busy while the new slice's first
+// fragments come from LDS.  The order of the MFMAs on each accumulator is
+// unchanged.
 template <Operand OA, Operand OB, typename SA, typename SB>
 __device__ __forceinline__ void gemm_tile(FA_LDS char* smem, int nk, SA&& stage_a, SB&& stage_b,
                                           f32x16 (&acc)[MB][NB], int wave, int lane) {
