@@ -207,6 +207,55 @@ def test_seeded_sweep(case):
     _compare(out, _oracle_full(t, seg, scale, causal), c["dtype"])
 
 
+def _wide_cases(n=64, seed=777):
+    """A second seeded list, wider than the first: up to 16 heads and groups
+    of 8, lengths up to 1100 (ragged, whole 64-key tiles and 256-row
+    workgroups +-2), segments of 1, 2, 7, 33, 64, 65 or 200 tokens or the
+    whole row, softmax scales of 0.5, 1 and 2 times 1/sqrt(D), and, for bf16,
+    queries 3 or 6 times larger (scores up to 12 times steeper)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 3, 4]))
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        while Hkv * G > 16:
+            G //= 2
+        N = max(1, int(rng.choice([int(rng.integers(1, 1100)), 64 * int(rng.integers(1, 17)),
+                                   256 * int(rng.integers(1, 5)) + int(rng.integers(-2, 3))])))
+        dtype = str(rng.choice(["bf16", "bf16", "fp32"]))
+        cases.append(dict(B=int(rng.integers(1, 3)), H=Hkv * G, Hkv=Hkv, N=N, D=int(rng.choice([64, 96, 128])),
+                          dtype=dtype, mode=str(rng.choice(list(MODES))),
+                          max_len=int(rng.choice([1, 2, 7, 33, 64, 65, 200, N])),
+                          qmul=float(rng.choice([1.0, 3.0, 6.0])) if dtype == "bf16" else 1.0,
+                          scale_mul=float(rng.choice([0.5, 1.0, 2.0])), seed=90000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _wide_cases(),
+                         ids=lambda c: "B{B}H{H}Hkv{Hkv}N{N}D{D}{dtype}{mode}L{max_len}q{qmul:g}s{scale_mul:g}".format(**c))
+def test_seeded_wide_sweep(case):
+    """The wider mixed configurations against the full oracle.  Where the
+    scores are steeper than 1.5 times the usual scale in bf16, dQ and dK are
+    not compared (the reading of test_rising_and_falling_scores: dS is then
+    rounding noise of dP - D_i on both sides); O, LSE and dV are."""
+    c = case
+    packed, causal = MODES[c["mode"]]
+    say(f"wide sweep {c}")
+    t = workloads.make_tensors(c["B"], c["H"], c["N"], c["D"], c["dtype"], c["seed"], Hkv=c["Hkv"])
+    if c["qmul"] != 1.0:
+        t["q"] = workloads.bf16_round(t["q"] * c["qmul"])
+    seg = workloads.random_segments(c["B"], c["N"], c["seed"], max_len=c["max_len"]) if packed else None
+    scale = c["scale_mul"] / np.sqrt(c["D"])
+    out = run_gpu(t, seg, c["dtype"], scale, causal)
+    ref = _oracle_full(t, seg, scale, causal)
+    if c["dtype"] == "bf16" and c["qmul"] * c["scale_mul"] > 1.5:
+        check_o(down(out["o"]), ref["o"], "bf16", pv_abs=ref["pv"])
+        check_lse(down(out["lse"]), ref["lse"], "bf16")
+        check_grad(down(out["dv"]), ref["dv"], "bf16", "dv")
+    else:
+        _compare(out, ref, c["dtype"])
+
+
 # ---------------------------------------------------------------- the workloads
 
 def test_tiny_fp32_one_segment():
