@@ -83,6 +83,27 @@ def test_lce_small_shapes(N, V, D):
         assert e <= REL_L2, f"{name}: relative L2 {e:.3e}"
 
 
+def test_lce_steep_logits():
+    """Hidden states 30 times larger: logits of standard deviation 30, row
+    maxima near 100, where exp(z) overflows fp32 unless every vocabulary tile
+    and every fold of tiles subtracts its maximum first."""
+    N, V, D = 300, 5000, 256
+    say(f"lce steep logits N{N} V{V} D{D}")
+    x = workloads.make_lce_inputs(N, V, D, seed=31, targets_edge=True)
+    x["h"] = workloads.bf16_round(x["h"] * 30.0)
+    out = _run(x)
+    nll, lse, tz = lce_forward(x["h"], x["w"], x["targets"])
+    dh, dw = lce_backward(x["h"], x["w"], x["targets"], x["dnll"])
+    assert np.abs(lse).max() > 88.0, "the case must reach logits whose exp overflows fp32"
+    _check_abs("nll", down(out["nll"]), nll)
+    _check_abs("lse", down(out["lse"]), lse)
+    _check_abs("tlogit", down(out["tz"]), tz)
+    for name, g, r in (("dh", down(out["dh"]), dh), ("dw", down(out["dw"]), dw)):
+        e = rel_l2(g, r)
+        say(f"  {name} rel-L2 {e:.2e}")
+        assert e <= REL_L2, f"{name}: relative L2 {e:.3e}"
+
+
 def test_lce_frozen_head_skips_dw():
     x = workloads.make_lce_inputs(40, 500, 256, seed=9)
     a = _run(x, need_dw=False)
